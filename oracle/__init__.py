@@ -1,0 +1,11 @@
+"""fp64 CPU oracle for paged decode attention — TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may
+import this package.  The library under ``paged_kv_cache_203_amd`` never imports it, and the two
+share no code: the oracle is a plain, slow restatement of the definitions, written in NumPy
+float64, so that a reader can check it against the pages by eye.
+"""
+from .paged_attention import (to_f64, gather_rows, paged_decode_attention,  # noqa: F401
+                              paged_decode_attention_partial, num_partitions, lse_merge,
+                              paged_kv_append, validate_metadata, STATUS_PAGE_RANGE,
+                              STATUS_CAPACITY, STATUS_APPEND_ALIAS)
