@@ -1,0 +1,163 @@
+/*
+ * pkv.h — C ABI of libpkv: single-token grouped-query decode attention over a paged KV cache,
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The operation.  Each sequence b of a decode batch has one new query token q[b] (Hq heads of
+ * head_dim D) and a context of L_b earlier tokens whose key and value rows live in fixed-size
+ * pages of one shared pool.  Logical token t of sequence b is slot t % page_size of physical page
+ * page_table[b][t / page_size].  Query head h attends with KV head h / (Hq / Hkv) (grouped-query
+ * attention), and the result is softmax(scale * q K^T) V over the L_b tokens.
+ *   - CacheIR page, "Compiler Example": decode lowers grouped_query_attention to one
+ *     paged_attention_decode(q, k, v) call that receives the new token's k and v.
+ *   - CacheIR page, "Current Capabilities" / "Boundaries": paged KV metadata over persistent
+ *     shared page-backed KV pools, page-table decode attention with GQA mapping, a batched
+ *     paged-attention ABI and a reduced (split-then-reduce) paged-attention decode.
+ *   - TorchInferno page, "Custom Kernels": paged_decode_attention and
+ *     batched_paged_decode_attention (one page table per request); "Runtime Scaffolds":
+ *     runtime.paged holds page-table-shaped KV allocation; "OpenAI-Compatible Serving": separate
+ *     KV-append, grouped decode and streaming (blockwise) decode kernels.
+ *   - Sequences that share a prefix name the same physical pages in their tables (TorchInferno
+ *     page, "Design Coverage": shared prefix-page reuse).
+ *
+ * Layouts (all row-major, contiguous, element type = pkv_shape.dtype unless stated):
+ *   q            [batch, num_q_heads, head_dim]
+ *   k_pool       [num_pages, page_size, num_kv_heads, head_dim]   (v_pool the same)
+ *   page_table   int32 [batch, max_pages_per_seq]
+ *   context_lens int32 [batch]
+ *   out          [batch, num_q_heads, head_dim]          (same dtype as q)
+ *   partial_out  float32 [batch, num_q_heads, max_partitions, head_dim]
+ *   partial_lse  float32 [batch, num_q_heads, max_partitions]  (natural-log log-sum-exp)
+ *   k_new, v_new [batch, num_kv_heads, head_dim]
+ *
+ * Ownership and ordering.  Every pointer argument (except `shape`, which is host memory read
+ * during the call) is device memory owned by the caller.  The library allocates nothing, keeps
+ * no pointer after returning, and only enqueues work on `stream` (a hipStream_t; NULL is the
+ * null stream) without synchronising, except pkv_validate_metadata, which documents its own
+ * behaviour.  The caller keeps buffers alive and unmodified until the enqueued work completes.
+ * Device metadata is never modified.
+ *
+ * Errors.  Every call checks its arguments on the host before enqueuing anything and returns
+ *   PKV_OK (0), PKV_EINVAL (-1, a bad argument), PKV_EUNSUPPORTED (-2, valid but not built:
+ *   dtype, head_dim, page_size, group size), PKV_ELAUNCH (-3, the HIP launch failed) or
+ *   PKV_EWORKSPACE (-4, a caller buffer too small).
+ * On a non-zero return nothing was enqueued (PKV_ELAUNCH aside) and pkv_last_error() returns a
+ * message for the calling thread.  There is no fallback path.
+ *
+ * Supported: dtype f32 / bf16 / f16; head_dim 64 or 128; page_size a power of two from 16 to
+ * 256; num_q_heads a multiple of num_kv_heads with group size G = Hq / Hkv at most 16.
+ *
+ * Device-side metadata preconditions (page ids of live entries in [0, num_pages),
+ * context_lens[b] <= max_pages_per_seq * page_size) cannot be read on the host without a sync;
+ * pkv_validate_metadata checks them.  The kernels never read or write outside the pools when
+ * they are violated: a row whose live page id is out of range, or whose length exceeds the
+ * table's capacity, gets NaN outputs (attention) or is skipped (append).
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_OK 0
+#define PKV_EINVAL (-1)
+#define PKV_EUNSUPPORTED (-2)
+#define PKV_ELAUNCH (-3)
+#define PKV_EWORKSPACE (-4)
+
+typedef enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_F16 = 2 } pkv_dtype;
+
+/* Sizes shared by every call.  Element type `dtype` (a pkv_dtype) applies to q, the pools,
+ * k_new, v_new and out. */
+typedef struct {
+  int32_t batch;              /* B >= 0 (0: nothing to do)                          */
+  int32_t num_q_heads;        /* Hq > 0, a multiple of num_kv_heads                 */
+  int32_t num_kv_heads;       /* Hkv > 0                                            */
+  int32_t head_dim;           /* D: 64 or 128                                       */
+  int32_t page_size;          /* PS: power of two, 16..256                          */
+  int32_t num_pages;          /* NP > 0: pages in each pool                         */
+  int32_t max_pages_per_seq;  /* MP > 0: page_table row length                      */
+  int32_t dtype;              /* pkv_dtype                                          */
+} pkv_shape;
+
+/* Decode attention, one pass per (sequence, KV head).
+ *
+ * out[b, h, :] = sum_t softmax_t(scale * q[b,h] . K_b[t, h/G]) V_b[t, h/G, :] for t < L_b,
+ * where K_b/V_b are the rows reached through page_table[b] and L_b = context_lens[b].
+ * Accumulation is float32; out is rounded to the element type (round-to-nearest-even).
+ * context_lens[b] <= 0 gives out[b] = 0.  Table entries past ceil(L_b / PS) and slots at or past
+ * L_b in the last page are never read.  `scale` must be finite (usually 1/sqrt(D)).
+ * `out` must not overlap q or the pools. */
+int pkv_paged_decode_attention(const void* q, const void* k_pool, const void* v_pool,
+                               const int32_t* page_table, const int32_t* context_lens,
+                               float scale, void* out, const pkv_shape* shape, void* stream);
+
+/* Split-KV (flash-decoding) partial attention.
+ *
+ * Partition p of sequence b covers logical tokens [p*P, min((p+1)*P, L_b)) with
+ * P = partition_tokens (a multiple of page_size).  For every p < ceil(L_b / P) it writes the
+ * normalised partial output partial_out[b, h, p, :] (float32) and its log-sum-exp
+ * partial_lse[b, h, p] = ln sum_t exp(scale * q . k_t) over the partition.  Partitions at or past
+ * ceil(L_b / P) are not written.  max_partitions (the third dimension of both buffers) must be at
+ * least ceil(max_pages_per_seq * page_size / P), else PKV_EWORKSPACE.  Results depend only on
+ * the sequence's own tokens and P, never on the batch around it.  This follows the "reduced
+ * paged-attention decode" of the CacheIR page ("Current Capabilities") and the blockwise
+ * streaming decode of the TorchInferno page ("OpenAI-Compatible Serving"); the split itself is
+ * the flash-decoding form. */
+int pkv_paged_decode_attention_partial(const void* q, const void* k_pool, const void* v_pool,
+                                       const int32_t* page_table, const int32_t* context_lens,
+                                       float scale, int32_t partition_tokens,
+                                       float* partial_out, float* partial_lse,
+                                       int32_t max_partitions, const pkv_shape* shape,
+                                       void* stream);
+
+/* Log-sum-exp merge of the partitions written by pkv_paged_decode_attention_partial.
+ *
+ * With n_b = ceil(L_b / P) partitions, M = max_p lse_p and w_p = exp(lse_p - M):
+ *   out[b, h, :] = sum_p w_p partial_out[b, h, p, :] / sum_p w_p   (rounded to the element type)
+ *   lse_out[b, h] = M + ln sum_p w_p                               (float32; lse_out may be NULL)
+ * Rows with L_b <= 0 get out = 0 and lse_out = -inf.  `out` must not overlap the partials. */
+int pkv_lse_merge(const float* partial_out, const float* partial_lse,
+                  const int32_t* context_lens, int32_t partition_tokens, int32_t max_partitions,
+                  void* out, float* lse_out, const pkv_shape* shape, void* stream);
+
+/* Paged KV append: the new token's key and value rows of every sequence are copied, bit for
+ * bit, into the pools at logical position L_b = context_lens[b] (the pre-append length), i.e.
+ * slot L_b % PS of page page_table[b][L_b / PS].  Rows with context_lens[b] < 0 are padding and
+ * write nothing.  No other byte of the pools changes; re-running it writes the same bytes.
+ * Attention afterwards is called with context_lens + 1.  Destinations must be distinct across
+ * rows and must not be a page another row reads (check with pkv_validate_metadata); padding rows
+ * never write.  (CacheIR page, "Compiler Example": the decode op receives the new k and v;
+ * TorchInferno page, "OpenAI-Compatible Serving": the KV-append kernel.) */
+int pkv_paged_kv_append(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                        const int32_t* page_table, const int32_t* context_lens,
+                        const pkv_shape* shape, void* stream);
+
+/* Device-side check of the metadata preconditions.  Rows with L = context_lens[b] +
+ * extra_tokens > 0 are live and use n = ceil(L / PS) table entries.  Writes one int32 status
+ * word to device_status (stream-ordered; read it after the stream completes):
+ *   bit 0 (1): a live table entry outside [0, num_pages)
+ *   bit 1 (2): n > max_pages_per_seq (the length exceeds the table's capacity)
+ *   bit 2 (4): with check_append_unique != 0, a row's append page (entry context_lens[b] / PS)
+ *              is also a live entry of another row. */
+int pkv_validate_metadata(const int32_t* page_table, const int32_t* context_lens,
+                          int32_t extra_tokens, int32_t check_append_unique,
+                          int32_t* device_status, const pkv_shape* shape, void* stream);
+
+/* Bytes of partial_out plus partial_lse for `max_partitions` partitions (0 on a bad shape). */
+size_t pkv_partial_workspace_bytes(const pkv_shape* shape, int32_t max_partitions);
+
+/* Message describing the calling thread's last non-zero return ("" if none). */
+const char* pkv_last_error(void);
+
+/* Library version string. */
+const char* pkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -1,0 +1,185 @@
+// C-ABI entry points of libpkv (declared in include/pkv.h): host-side checks, then one launch on
+// the caller's stream.  No allocation, no synchronisation, no state kept between calls.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <string>
+
+#include "../../include/pkv.h"
+#include "pkv_check.h"
+#include "pkv_launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int set_error(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+int log2_exact(int32_t x) {
+  int s = 0;
+  while ((1 << s) < x) ++s;
+  return s;
+}
+
+int group_pad(int g) { return g <= 4 ? 4 : (g <= 8 ? 8 : 16); }
+
+int launch_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return PKV_OK;
+  return set_error(PKV_ELAUNCH, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+pkv::DecodeParams decode_params(const void* q, const void* k_pool, const void* v_pool,
+                                const int32_t* page_table, const int32_t* context_lens,
+                                float scale, const pkv_shape& s) {
+  pkv::DecodeParams p{};
+  const int e = pkv::elem_bytes(s.dtype);
+  p.q = q;
+  p.k_pool = k_pool;
+  p.v_pool = v_pool;
+  p.page_table = page_table;
+  p.context_lens = context_lens;
+  p.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634074);
+  p.batch = s.batch;
+  p.hq = s.num_q_heads;
+  p.hkv = s.num_kv_heads;
+  p.group = s.num_q_heads / s.num_kv_heads;
+  p.num_pages = s.num_pages;
+  p.max_pages = s.max_pages_per_seq;
+  p.page_shift = log2_exact(s.page_size);
+  p.capacity = s.max_pages_per_seq * s.page_size;
+  p.tok_stride = s.num_kv_heads * s.head_dim * e;
+  p.page_stride = int64_t(s.page_size) * p.tok_stride;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_last_error(void) { return g_last_error.c_str(); }
+
+const char* pkv_version(void) { return "pkv 0.1.0 gfx950"; }
+
+size_t pkv_partial_workspace_bytes(const pkv_shape* shape, int32_t max_partitions) {
+  std::string msg;
+  if (pkv::check_shape(shape, msg) != PKV_OK || max_partitions <= 0) return 0;
+  const uint64_t rows = uint64_t(shape->batch) * shape->num_q_heads * uint64_t(max_partitions);
+  return size_t(rows * shape->head_dim * 4 + rows * 4);
+}
+
+int pkv_paged_decode_attention(const void* q, const void* k_pool, const void* v_pool,
+                               const int32_t* page_table, const int32_t* context_lens,
+                               float scale, void* out, const pkv_shape* shape, void* stream) {
+  std::string msg;
+  const int rc = pkv::check_decode(q, k_pool, v_pool, page_table, context_lens, scale, out, shape, msg);
+  if (rc) return set_error(rc, "pkv_paged_decode_attention: " + msg);
+  if (shape->batch == 0) return PKV_OK;
+  pkv::DecodeParams p = decode_params(q, k_pool, v_pool, page_table, context_lens, scale, *shape);
+  p.out = out;
+  p.partition_tokens = p.capacity;
+  p.max_partitions = 1;
+  (void)hipGetLastError();
+  return launch_status(pkv::launch_decode(p, shape->dtype, shape->head_dim, group_pad(p.group),
+                                          false, static_cast<hipStream_t>(stream)),
+                       "pkv_paged_decode_attention");
+}
+
+int pkv_paged_decode_attention_partial(const void* q, const void* k_pool, const void* v_pool,
+                                       const int32_t* page_table, const int32_t* context_lens,
+                                       float scale, int32_t partition_tokens,
+                                       float* partial_out, float* partial_lse,
+                                       int32_t max_partitions, const pkv_shape* shape,
+                                       void* stream) {
+  std::string msg;
+  const int rc = pkv::check_partial(q, k_pool, v_pool, page_table, context_lens, scale,
+                                    partition_tokens, partial_out, partial_lse, max_partitions,
+                                    shape, msg);
+  if (rc) return set_error(rc, "pkv_paged_decode_attention_partial: " + msg);
+  if (shape->batch == 0) return PKV_OK;
+  pkv::DecodeParams p = decode_params(q, k_pool, v_pool, page_table, context_lens, scale, *shape);
+  p.partial_out = partial_out;
+  p.partial_lse = partial_lse;
+  p.partition_tokens = partition_tokens;
+  p.max_partitions = max_partitions;
+  (void)hipGetLastError();
+  return launch_status(pkv::launch_decode(p, shape->dtype, shape->head_dim, group_pad(p.group),
+                                          true, static_cast<hipStream_t>(stream)),
+                       "pkv_paged_decode_attention_partial");
+}
+
+int pkv_lse_merge(const float* partial_out, const float* partial_lse,
+                  const int32_t* context_lens, int32_t partition_tokens, int32_t max_partitions,
+                  void* out, float* lse_out, const pkv_shape* shape, void* stream) {
+  std::string msg;
+  const int rc = pkv::check_merge(partial_out, partial_lse, context_lens, partition_tokens,
+                                  max_partitions, out, lse_out, shape, msg);
+  if (rc) return set_error(rc, "pkv_lse_merge: " + msg);
+  if (shape->batch == 0) return PKV_OK;
+  pkv::MergeParams p{};
+  p.partial_out = partial_out;
+  p.partial_lse = partial_lse;
+  p.context_lens = context_lens;
+  p.out = out;
+  p.lse_out = lse_out;
+  p.batch = shape->batch;
+  p.hq = shape->num_q_heads;
+  p.partition_tokens = partition_tokens;
+  p.max_partitions = max_partitions;
+  p.capacity = shape->max_pages_per_seq * shape->page_size;
+  (void)hipGetLastError();
+  return launch_status(pkv::launch_merge(p, shape->dtype, shape->head_dim,
+                                         static_cast<hipStream_t>(stream)),
+                       "pkv_lse_merge");
+}
+
+int pkv_paged_kv_append(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                        const int32_t* page_table, const int32_t* context_lens,
+                        const pkv_shape* shape, void* stream) {
+  std::string msg;
+  const int rc = pkv::check_append(k_new, v_new, k_pool, v_pool, page_table, context_lens, shape, msg);
+  if (rc) return set_error(rc, "pkv_paged_kv_append: " + msg);
+  if (shape->batch == 0) return PKV_OK;
+  pkv::AppendParams p{};
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.k_pool = k_pool;
+  p.v_pool = v_pool;
+  p.page_table = page_table;
+  p.context_lens = context_lens;
+  p.batch = shape->batch;
+  p.num_pages = shape->num_pages;
+  p.max_pages = shape->max_pages_per_seq;
+  p.page_shift = log2_exact(shape->page_size);
+  p.capacity = shape->max_pages_per_seq * shape->page_size;
+  p.row_bytes = shape->num_kv_heads * shape->head_dim * pkv::elem_bytes(shape->dtype);
+  p.page_stride = int64_t(shape->page_size) * p.row_bytes;
+  (void)hipGetLastError();
+  return launch_status(pkv::launch_append(p, static_cast<hipStream_t>(stream)),
+                       "pkv_paged_kv_append");
+}
+
+int pkv_validate_metadata(const int32_t* page_table, const int32_t* context_lens,
+                          int32_t extra_tokens, int32_t check_append_unique,
+                          int32_t* device_status, const pkv_shape* shape, void* stream) {
+  std::string msg;
+  const int rc = pkv::check_validate(page_table, context_lens, extra_tokens, device_status, shape, msg);
+  if (rc) return set_error(rc, "pkv_validate_metadata: " + msg);
+  pkv::ValidateParams p{};
+  p.page_table = page_table;
+  p.context_lens = context_lens;
+  p.device_status = device_status;
+  p.batch = shape->batch;
+  p.num_pages = shape->num_pages;
+  p.max_pages = shape->max_pages_per_seq;
+  p.page_size = shape->page_size;
+  p.extra_tokens = extra_tokens;
+  p.check_append_unique = check_append_unique ? 1 : 0;
+  (void)hipGetLastError();
+  return launch_status(pkv::launch_validate(p, static_cast<hipStream_t>(stream)),
+                       "pkv_validate_metadata");
+}
+
+}  // extern "C"

@@ -1,0 +1,216 @@
+// Host-side argument checks (see pkv_check.h).  Every check runs before anything is enqueued:
+// unsupported layouts, misaligned or aliased buffers and undersized workspaces are rejected up
+// front rather than silently handled another way.
+#include "pkv_check.h"
+
+#include <cmath>
+#include <cstdio>
+
+namespace pkv {
+
+namespace {
+
+int fail(std::string& msg, int code, const char* text) {
+  msg = text;
+  return code;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool is_pow2(int32_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+}  // namespace
+
+int elem_bytes(int32_t dtype) {
+  switch (dtype) {
+    case PKV_F32: return 4;
+    case PKV_BF16: return 2;
+    case PKV_F16: return 2;
+    default: return 0;
+  }
+}
+
+int check_shape(const pkv_shape* s, std::string& msg) {
+  if (!s) return fail(msg, PKV_EINVAL, "shape is NULL");
+  if (s->batch < 0) return fail(msg, PKV_EINVAL, "batch must be >= 0");
+  if (s->num_q_heads <= 0 || s->num_kv_heads <= 0)
+    return fail(msg, PKV_EINVAL, "num_q_heads and num_kv_heads must be > 0");
+  if (s->num_q_heads % s->num_kv_heads != 0)
+    return fail(msg, PKV_EINVAL, "num_q_heads must be a multiple of num_kv_heads");
+  if (s->head_dim <= 0) return fail(msg, PKV_EINVAL, "head_dim must be > 0");
+  if (s->page_size <= 0) return fail(msg, PKV_EINVAL, "page_size must be > 0");
+  if (s->num_pages <= 0) return fail(msg, PKV_EINVAL, "num_pages must be > 0");
+  if (s->max_pages_per_seq <= 0) return fail(msg, PKV_EINVAL, "max_pages_per_seq must be > 0");
+  if (elem_bytes(s->dtype) == 0) return fail(msg, PKV_EUNSUPPORTED, "dtype must be f32, bf16 or f16");
+  if (s->head_dim != 64 && s->head_dim != 128)
+    return fail(msg, PKV_EUNSUPPORTED, "head_dim must be 64 or 128");
+  if (!is_pow2(s->page_size) || s->page_size < 16 || s->page_size > 256)
+    return fail(msg, PKV_EUNSUPPORTED, "page_size must be a power of two in [16, 256]");
+  if (s->num_q_heads / s->num_kv_heads > 16)
+    return fail(msg, PKV_EUNSUPPORTED, "group size num_q_heads / num_kv_heads must be <= 16");
+  // Tokens addressable by one row, and the largest in-page byte offset, must fit in int32.
+  const int64_t row_tokens = int64_t(s->max_pages_per_seq) * s->page_size;
+  if (row_tokens > INT32_MAX) return fail(msg, PKV_EINVAL, "max_pages_per_seq * page_size overflows int32");
+  const int64_t page_bytes =
+      int64_t(s->page_size) * s->num_kv_heads * s->head_dim * elem_bytes(s->dtype);
+  if (page_bytes > INT32_MAX) return fail(msg, PKV_EUNSUPPORTED, "one page exceeds 2 GiB");
+  if (int64_t(s->batch) * s->num_q_heads > INT32_MAX / 2)
+    return fail(msg, PKV_EINVAL, "batch * num_q_heads too large");
+  return PKV_OK;
+}
+
+Extents extents(const pkv_shape& s) {
+  const uint64_t e = uint64_t(elem_bytes(s.dtype));
+  Extents x;
+  x.q = uint64_t(s.batch) * s.num_q_heads * s.head_dim * e;
+  x.out = x.q;
+  x.pool = uint64_t(s.num_pages) * s.page_size * s.num_kv_heads * s.head_dim * e;
+  x.new_rows = uint64_t(s.batch) * s.num_kv_heads * s.head_dim * e;
+  x.table = uint64_t(s.batch) * s.max_pages_per_seq * 4;
+  x.lens = uint64_t(s.batch) * 4;
+  return x;
+}
+
+bool overlaps(const void* a, uint64_t na, const void* b, uint64_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+  return pa < pb + nb && pb < pa + na;
+}
+
+static int check_attention_inputs(const void* q, const void* k_pool, const void* v_pool,
+                                  const int32_t* page_table, const int32_t* context_lens,
+                                  float scale, std::string& msg) {
+  if (!q || !k_pool || !v_pool || !page_table || !context_lens)
+    return fail(msg, PKV_EINVAL, "q, k_pool, v_pool, page_table and context_lens must be non-NULL");
+  if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16))
+    return fail(msg, PKV_EUNSUPPORTED, "q, k_pool and v_pool must be 16-byte aligned");
+  if (!aligned(page_table, 4) || !aligned(context_lens, 4))
+    return fail(msg, PKV_EINVAL, "page_table and context_lens must be 4-byte aligned");
+  if (!std::isfinite(scale)) return fail(msg, PKV_EINVAL, "scale must be finite");
+  return PKV_OK;
+}
+
+int check_decode(const void* q, const void* k_pool, const void* v_pool, const int32_t* page_table,
+                 const int32_t* context_lens, float scale, const void* out, const pkv_shape* s,
+                 std::string& msg) {
+  int rc = check_shape(s, msg);
+  if (rc) return rc;
+  if (s->batch == 0) return PKV_OK;
+  rc = check_attention_inputs(q, k_pool, v_pool, page_table, context_lens, scale, msg);
+  if (rc) return rc;
+  if (!out) return fail(msg, PKV_EINVAL, "out must be non-NULL");
+  if (!aligned(out, 16)) return fail(msg, PKV_EUNSUPPORTED, "out must be 16-byte aligned");
+  const Extents x = extents(*s);
+  if (overlaps(out, x.out, q, x.q) || overlaps(out, x.out, k_pool, x.pool) ||
+      overlaps(out, x.out, v_pool, x.pool) || overlaps(out, x.out, page_table, x.table) ||
+      overlaps(out, x.out, context_lens, x.lens))
+    return fail(msg, PKV_EINVAL, "out overlaps an input");
+  return PKV_OK;
+}
+
+int32_t partitions_needed(const pkv_shape& s, int32_t partition_tokens) {
+  const int64_t row_tokens = int64_t(s.max_pages_per_seq) * s.page_size;
+  return int32_t((row_tokens + partition_tokens - 1) / partition_tokens);
+}
+
+int check_partial(const void* q, const void* k_pool, const void* v_pool, const int32_t* page_table,
+                  const int32_t* context_lens, float scale, int32_t partition_tokens,
+                  const float* partial_out, const float* partial_lse, int32_t max_partitions,
+                  const pkv_shape* s, std::string& msg) {
+  int rc = check_shape(s, msg);
+  if (rc) return rc;
+  if (partition_tokens <= 0 || partition_tokens % s->page_size != 0)
+    return fail(msg, PKV_EINVAL, "partition_tokens must be a positive multiple of page_size");
+  if (max_partitions <= 0) return fail(msg, PKV_EINVAL, "max_partitions must be > 0");
+  if (max_partitions < partitions_needed(*s, partition_tokens))
+    return fail(msg, PKV_EWORKSPACE,
+                "max_partitions < ceil(max_pages_per_seq * page_size / partition_tokens)");
+  if (s->batch == 0) return PKV_OK;
+  rc = check_attention_inputs(q, k_pool, v_pool, page_table, context_lens, scale, msg);
+  if (rc) return rc;
+  if (!partial_out || !partial_lse)
+    return fail(msg, PKV_EINVAL, "partial_out and partial_lse must be non-NULL");
+  if (!aligned(partial_out, 16) || !aligned(partial_lse, 4))
+    return fail(msg, PKV_EUNSUPPORTED, "partial_out must be 16-byte and partial_lse 4-byte aligned");
+  const Extents x = extents(*s);
+  const uint64_t rows = uint64_t(s->batch) * s->num_q_heads * uint64_t(max_partitions);
+  const uint64_t po = rows * s->head_dim * 4, pl = rows * 4;
+  const void* ins[5] = {q, k_pool, v_pool, page_table, context_lens};
+  const uint64_t ins_n[5] = {x.q, x.pool, x.pool, x.table, x.lens};
+  for (int i = 0; i < 5; ++i)
+    if (overlaps(partial_out, po, ins[i], ins_n[i]) || overlaps(partial_lse, pl, ins[i], ins_n[i]))
+      return fail(msg, PKV_EINVAL, "partial buffers overlap an input");
+  if (overlaps(partial_out, po, partial_lse, pl))
+    return fail(msg, PKV_EINVAL, "partial_out overlaps partial_lse");
+  return PKV_OK;
+}
+
+int check_merge(const float* partial_out, const float* partial_lse, const int32_t* context_lens,
+                int32_t partition_tokens, int32_t max_partitions, const void* out,
+                const float* lse_out, const pkv_shape* s, std::string& msg) {
+  int rc = check_shape(s, msg);
+  if (rc) return rc;
+  if (partition_tokens <= 0 || partition_tokens % s->page_size != 0)
+    return fail(msg, PKV_EINVAL, "partition_tokens must be a positive multiple of page_size");
+  if (max_partitions <= 0) return fail(msg, PKV_EINVAL, "max_partitions must be > 0");
+  if (max_partitions < partitions_needed(*s, partition_tokens))
+    return fail(msg, PKV_EWORKSPACE,
+                "max_partitions < ceil(max_pages_per_seq * page_size / partition_tokens)");
+  if (s->batch == 0) return PKV_OK;
+  if (!partial_out || !partial_lse || !context_lens || !out)
+    return fail(msg, PKV_EINVAL, "partial_out, partial_lse, context_lens and out must be non-NULL");
+  if (!aligned(partial_out, 16) || !aligned(out, 16))
+    return fail(msg, PKV_EUNSUPPORTED, "partial_out and out must be 16-byte aligned");
+  if (!aligned(partial_lse, 4) || !aligned(context_lens, 4) || (lse_out && !aligned(lse_out, 4)))
+    return fail(msg, PKV_EINVAL, "partial_lse, context_lens and lse_out must be 4-byte aligned");
+  const Extents x = extents(*s);
+  const uint64_t rows = uint64_t(s->batch) * s->num_q_heads * uint64_t(max_partitions);
+  const uint64_t po = rows * s->head_dim * 4, pl = rows * 4;
+  const uint64_t lo = uint64_t(s->batch) * s->num_q_heads * 4;
+  if (overlaps(out, x.out, partial_out, po) || overlaps(out, x.out, partial_lse, pl) ||
+      overlaps(out, x.out, context_lens, x.lens))
+    return fail(msg, PKV_EINVAL, "out overlaps an input");
+  if (lse_out && (overlaps(lse_out, lo, partial_out, po) || overlaps(lse_out, lo, partial_lse, pl) ||
+                  overlaps(lse_out, lo, out, x.out) || overlaps(lse_out, lo, context_lens, x.lens)))
+    return fail(msg, PKV_EINVAL, "lse_out overlaps another buffer");
+  return PKV_OK;
+}
+
+int check_append(const void* k_new, const void* v_new, const void* k_pool, const void* v_pool,
+                 const int32_t* page_table, const int32_t* context_lens, const pkv_shape* s,
+                 std::string& msg) {
+  int rc = check_shape(s, msg);
+  if (rc) return rc;
+  if (s->batch == 0) return PKV_OK;
+  if (!k_new || !v_new || !k_pool || !v_pool || !page_table || !context_lens)
+    return fail(msg, PKV_EINVAL, "every pointer must be non-NULL");
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16))
+    return fail(msg, PKV_EUNSUPPORTED, "k_new, v_new and the pools must be 16-byte aligned");
+  if (!aligned(page_table, 4) || !aligned(context_lens, 4))
+    return fail(msg, PKV_EINVAL, "page_table and context_lens must be 4-byte aligned");
+  const Extents x = extents(*s);
+  if (overlaps(k_pool, x.pool, v_pool, x.pool)) return fail(msg, PKV_EINVAL, "k_pool overlaps v_pool");
+  const void* ins[4] = {k_new, v_new, page_table, context_lens};
+  const uint64_t ins_n[4] = {x.new_rows, x.new_rows, x.table, x.lens};
+  for (int i = 0; i < 4; ++i)
+    if (overlaps(k_pool, x.pool, ins[i], ins_n[i]) || overlaps(v_pool, x.pool, ins[i], ins_n[i]))
+      return fail(msg, PKV_EINVAL, "a pool overlaps an input of the append");
+  return PKV_OK;
+}
+
+int check_validate(const int32_t* page_table, const int32_t* context_lens, int32_t extra_tokens,
+                   const int32_t* device_status, const pkv_shape* s, std::string& msg) {
+  int rc = check_shape(s, msg);
+  if (rc) return rc;
+  if (extra_tokens < 0) return fail(msg, PKV_EINVAL, "extra_tokens must be >= 0");
+  if (!device_status) return fail(msg, PKV_EINVAL, "device_status must be non-NULL");
+  if (!aligned(device_status, 4)) return fail(msg, PKV_EINVAL, "device_status must be 4-byte aligned");
+  if (s->batch == 0) return PKV_OK;
+  if (!page_table || !context_lens)
+    return fail(msg, PKV_EINVAL, "page_table and context_lens must be non-NULL");
+  if (!aligned(page_table, 4) || !aligned(context_lens, 4))
+    return fail(msg, PKV_EINVAL, "page_table and context_lens must be 4-byte aligned");
+  return PKV_OK;
+}
+
+}  // namespace pkv

@@ -1,0 +1,52 @@
+// Host-side argument checks for the libpkv entry points.  Pure C++ (no HIP), so the checks can
+// be built and unit-tested with any host compiler.  Each function returns a PKV_* code and, on
+// failure, a message in `msg`.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+
+#include "../../include/pkv.h"
+
+namespace pkv {
+
+// Element size in bytes of a pkv_dtype (0 if unknown).
+int elem_bytes(int32_t dtype);
+
+// Sizes every call shares: positive heads, Hq % Hkv == 0, supported D / PS / G / dtype.
+int check_shape(const pkv_shape* s, std::string& msg);
+
+// Byte extent of each tensor for a checked shape.
+struct Extents {
+  uint64_t q, pool, out, new_rows, table, lens;
+};
+Extents extents(const pkv_shape& s);
+
+// Range overlap of [a, a+na) and [b, b+nb).
+bool overlaps(const void* a, uint64_t na, const void* b, uint64_t nb);
+
+int check_decode(const void* q, const void* k_pool, const void* v_pool, const int32_t* page_table,
+                 const int32_t* context_lens, float scale, const void* out, const pkv_shape* s,
+                 std::string& msg);
+
+// Smallest max_partitions that covers every length the page table can address.
+int32_t partitions_needed(const pkv_shape& s, int32_t partition_tokens);
+
+int check_partial(const void* q, const void* k_pool, const void* v_pool, const int32_t* page_table,
+                  const int32_t* context_lens, float scale, int32_t partition_tokens,
+                  const float* partial_out, const float* partial_lse, int32_t max_partitions,
+                  const pkv_shape* s, std::string& msg);
+
+int check_merge(const float* partial_out, const float* partial_lse, const int32_t* context_lens,
+                int32_t partition_tokens, int32_t max_partitions, const void* out,
+                const float* lse_out, const pkv_shape* s, std::string& msg);
+
+int check_append(const void* k_new, const void* v_new, const void* k_pool, const void* v_pool,
+                 const int32_t* page_table, const int32_t* context_lens, const pkv_shape* s,
+                 std::string& msg);
+
+int check_validate(const int32_t* page_table, const int32_t* context_lens, int32_t extra_tokens,
+                   const int32_t* device_status, const pkv_shape* s, std::string& msg);
+
+}  // namespace pkv

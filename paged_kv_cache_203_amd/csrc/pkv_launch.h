@@ -1,0 +1,63 @@
+// Internal launch interface between the C-ABI layer (pkv_api.hip) and the kernels
+// (pkv_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+struct DecodeParams {
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* page_table;
+  const int32_t* context_lens;
+  void* out;             // single pass: [B, Hq, D] in the element type
+  float* partial_out;    // split: [B, Hq, max_partitions, D]
+  float* partial_lse;    // split: [B, Hq, max_partitions]
+  float scale_log2;      // scale * log2(e): scores are kept in the base-2 domain
+  int32_t batch, hq, hkv, group;
+  int32_t num_pages, max_pages, page_shift, capacity;   // capacity = max_pages * page_size
+  int32_t partition_tokens, max_partitions;
+  int32_t tok_stride;    // bytes between consecutive slots of a page (Hkv * D * elem)
+  int64_t page_stride;   // bytes per page (page_size * tok_stride)
+};
+
+struct MergeParams {
+  const float* partial_out;
+  const float* partial_lse;
+  const int32_t* context_lens;
+  void* out;
+  float* lse_out;        // may be null
+  int32_t batch, hq, partition_tokens, max_partitions, capacity;
+};
+
+struct AppendParams {
+  const void* k_new;
+  const void* v_new;
+  void* k_pool;
+  void* v_pool;
+  const int32_t* page_table;
+  const int32_t* context_lens;
+  int32_t batch, num_pages, max_pages, page_shift, capacity;
+  int32_t row_bytes;     // Hkv * D * elem: one slot of one pool
+  int64_t page_stride;
+};
+
+struct ValidateParams {
+  const int32_t* page_table;
+  const int32_t* context_lens;
+  int32_t* device_status;
+  int32_t batch, num_pages, max_pages, page_size, extra_tokens, check_append_unique;
+};
+
+// Each returns hipSuccess or the launch error.  `dtype` is a pkv_dtype; `group_pad` is the
+// padded GQA group (4, 8 or 16).
+hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim, int group_pad,
+                         bool partial, hipStream_t stream);
+hipError_t launch_merge(const MergeParams& p, int dtype, int head_dim, hipStream_t stream);
+hipError_t launch_append(const AppendParams& p, hipStream_t stream);
+hipError_t launch_validate(const ValidateParams& p, hipStream_t stream);
+
+}  // namespace pkv

@@ -1,0 +1,379 @@
+"""GPU parity: the HIP library against the fp64 oracle, through the C ABI.
+
+Bars (the oracle is exact float64; GPU accumulation is float32):
+  * max |out - oracle| <= 1e-5 for f32 KV and <= 2e-3 for bf16 / f16 KV;
+  * page-table handling and the append are bit-exact (address probes, raw-byte pool checks,
+    bitwise invariance under page relabelling, prefix unsharing, poisoning and batch composition).
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+from tests.helpers import (TOL, DeviceWorkload, assert_parity, log, to_device, to_f64,
+                           to_numpy_storage)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def pkv():
+    import paged_kv_cache_203_amd as lib
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return lib
+
+
+def oracle_out(w):
+    return O.paged_decode_attention(w.q, w.k_pool, w.v_pool, w.page_table, w.context_lens,
+                                    w.scale, w.dtype)
+
+
+def run_single(pkv, d):
+    return pkv.paged_decode_attention(d.q, d.k_pool, d.v_pool, d.page_table, d.context_lens, d.scale)
+
+
+def run_split(pkv, d, P):
+    return pkv.paged_decode_attention_split(d.q, d.k_pool, d.v_pool, d.page_table,
+                                            d.context_lens, P, d.scale)
+
+
+def small(i, **kw):
+    return W.make_workload(W.config(i).scaled(**kw))
+
+
+SMALL = {
+    1: dict(batch=1),
+    2: dict(batch=5, lengths=("uniform", 1, 300)),
+    3: dict(batch=6, lengths=("prefix", 64, 1, 70)),
+    4: dict(batch=7, lengths=("loguniform", 1, 400)),
+    5: dict(batch=3, lengths=("uniform", 100, 700)),
+}
+
+
+# ----------------------------------------------------------------------------------------------
+# parity at oracle-friendly sizes (several tiles, ragged tails), both entry points
+# ----------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("i", [1, 2, 3, 4, 5])
+def test_parity_small_single_and_split(pkv, i):
+    w = W.make_workload(W.config(i)) if i == 1 else small(i, **SMALL[i])
+    log(f"case config{i}-small shape={w.shape} lens={w.context_lens.tolist()[:8]}")
+    d = DeviceWorkload(w)
+    if w.cfg.append:
+        pkv.paged_kv_append(d.k_new, d.v_new, d.k_pool, d.v_pool, d.page_table, d.append_lens)
+        kp, vp = O.paged_kv_append(w.k_pool, w.v_pool, w.k_new, w.v_new, w.page_table, w.append_lens)
+        w.k_pool, w.v_pool = kp, vp
+    ref, _ = oracle_out(w)
+    out = run_single(pkv, d)
+    torch.cuda.synchronize()
+    assert_parity(to_f64(out), ref, w.dtype, f"config{i}-small single")
+    for P in (w.cfg.page_size, 64, 256):
+        if P % w.cfg.page_size:
+            continue
+        out = run_split(pkv, d, P)
+        torch.cuda.synchronize()
+        assert_parity(to_f64(out), ref, w.dtype, f"config{i}-small split P={P}")
+        # before any rounding to the element type: the merge can emit float32
+        po, pl = pkv.paged_decode_attention_partial(d.q, d.k_pool, d.v_pool, d.page_table,
+                                                    d.context_lens, P, d.scale)
+        o32 = pkv.lse_merge(po, pl, d.context_lens, P, w.cfg.page_size, w.page_table.shape[1],
+                            out=torch.empty(w.q.shape, dtype=torch.float32, device="cuda"))
+        torch.cuda.synchronize()
+        e32 = float(np.abs(to_f64(o32) - ref).max())
+        log(f"  float32 result before rounding, P={P}: max|err|={e32:.3e}")
+        assert e32 <= 1e-4
+
+
+@pytest.mark.parametrize("G,D,PS,dtype", [(1, 128, 16, "bf16"), (3, 64, 16, "bf16"),
+                                          (8, 128, 64, "f16"), (16, 128, 16, "bf16"),
+                                          (5, 64, 32, "f32"), (16, 64, 256, "f16"),
+                                          (2, 128, 128, "f32")])
+def test_parity_shapes(pkv, G, D, PS, dtype):
+    import dataclasses
+    cfg = dataclasses.replace(W.config(2), name=f"shape-G{G}-D{D}-PS{PS}-{dtype}", batch=4,
+                              num_q_heads=2 * G, num_kv_heads=2, head_dim=D, page_size=PS,
+                              dtype=dtype, lengths=("uniform", 1, 3 * PS + 40))
+    w = W.make_workload(cfg)
+    log(f"case {cfg.name} lens={w.context_lens.tolist()}")
+    d = DeviceWorkload(w)
+    ref, _ = oracle_out(w)
+    out = run_single(pkv, d)
+    torch.cuda.synchronize()
+    assert_parity(to_f64(out), ref, dtype, cfg.name + " single")
+    out = run_split(pkv, d, 2 * PS)
+    torch.cuda.synchronize()
+    assert_parity(to_f64(out), ref, dtype, cfg.name + " split")
+
+
+# ----------------------------------------------------------------------------------------------
+# full configurations
+# ----------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("i", [1, 2, 3, 4])
+def test_parity_full_config(pkv, i):
+    w = W.make_workload(W.config(i))
+    log(f"case config{i}-full shape={w.shape} tokens={w.logical_tokens()}")
+    d = DeviceWorkload(w)
+    if w.cfg.append:
+        pkv.paged_kv_append(d.k_new, d.v_new, d.k_pool, d.v_pool, d.page_table, d.append_lens)
+        kp, vp = O.paged_kv_append(w.k_pool, w.v_pool, w.k_new, w.v_new, w.page_table, w.append_lens)
+        assert np.array_equal(to_numpy_storage(d.k_pool, w.dtype).view(np.uint8), kp.view(np.uint8))
+        assert np.array_equal(to_numpy_storage(d.v_pool, w.dtype).view(np.uint8), vp.view(np.uint8))
+        w.k_pool, w.v_pool = kp, vp
+    ref, _ = oracle_out(w)
+    out = run_single(pkv, d)
+    torch.cuda.synchronize()
+    assert_parity(to_f64(out), ref, w.dtype, f"config{i} single", strict=True)
+    P = w.cfg.partition_tokens or 512
+    out = run_split(pkv, d, P)
+    torch.cuda.synchronize()
+    assert_parity(to_f64(out), ref, w.dtype, f"config{i} split P={P}", strict=True)
+
+
+def test_parity_full_config5_sampled_rows(pkv):
+    """Long-context split-KV at full size; the oracle checks a sample of rows one by one."""
+    w = W.make_workload(W.config(5))
+    log(f"case config5-full shape={w.shape} lens={w.context_lens.tolist()}")
+    d = DeviceWorkload(w)
+    P = w.cfg.partition_tokens
+    po, pl = pkv.paged_decode_attention_partial(d.q, d.k_pool, d.v_pool, d.page_table,
+                                                d.context_lens, P, d.scale)
+    out = pkv.lse_merge(po, pl, d.context_lens, P, w.cfg.page_size, w.page_table.shape[1],
+                        out=torch.empty_like(d.q))
+    single = run_single(pkv, d)
+    torch.cuda.synchronize()
+    got = to_f64(out)
+    got_single = to_f64(single)
+    rows = [int(np.argmin(w.context_lens)), int(np.argmax(w.context_lens))]
+    sub = W.subset_rows(w, rows)
+    ref, ref_lse = oracle_out(sub)
+    assert_parity(got[rows], ref, w.dtype, "config5 split (sampled rows)", strict=True)
+    assert_parity(got_single[rows], ref, w.dtype, "config5 single (sampled rows)", strict=True)
+    # partials of one sampled row against the oracle's partials
+    ref_po, ref_pl = O.paged_decode_attention_partial(sub.q, sub.k_pool, sub.v_pool, sub.page_table,
+                                                      sub.context_lens, sub.scale, sub.dtype, P)
+    n = int(O.num_partitions(sub.context_lens, P)[0])
+    gpo = po[rows[0]].double().cpu().numpy()[:, :n]
+    gpl = pl[rows[0]].double().cpu().numpy()[:, :n]
+    assert np.abs(gpo - ref_po[0, :, :n]).max() <= 1e-4
+    assert np.abs(gpl - ref_pl[0, :, :n]).max() <= 1e-4
+
+
+# ----------------------------------------------------------------------------------------------
+# split partials and the merge in isolation
+# ----------------------------------------------------------------------------------------------
+
+def test_partials_and_merge(pkv):
+    w = small(5, batch=4, lengths=("uniform", 1, 900))
+    w.context_lens[2] = 0
+    d = DeviceWorkload(w)
+    P = 128
+    po, pl = pkv.paged_decode_attention_partial(d.q, d.k_pool, d.v_pool, d.page_table,
+                                                d.context_lens, P, d.scale)
+    lse_out = torch.empty((4, w.cfg.num_q_heads), dtype=torch.float32, device="cuda")
+    out32 = pkv.lse_merge(po, pl, d.context_lens, P, w.cfg.page_size, w.page_table.shape[1],
+                          out=torch.empty(w.q.shape, dtype=torch.float32, device="cuda"), lse_out=lse_out)
+    torch.cuda.synchronize()
+    n = O.num_partitions(w.context_lens, P)
+    ref_po, ref_pl = O.paged_decode_attention_partial(w.q, w.k_pool, w.v_pool, w.page_table,
+                                                      w.context_lens, w.scale, w.dtype, P,
+                                                      max_partitions=po.shape[2])
+    gpo, gpl = po.double().cpu().numpy(), pl.double().cpu().numpy()
+    for b in range(4):
+        k = int(n[b])
+        assert np.abs(gpo[b, :, :k] - ref_po[b, :, :k]).max(initial=0) <= 1e-4
+        assert np.abs(gpl[b, :, :k] - ref_pl[b, :, :k]).max(initial=0) <= 1e-4
+    # the merge kernel against the fp64 merge of the GPU's own partials
+    mo, ml = O.lse_merge(gpo, gpl, n)
+    assert np.abs(to_f64(out32) - mo).max() <= 1e-5
+    gl = lse_out.double().cpu().numpy()
+    live = w.context_lens > 0
+    assert np.abs(gl[live] - ml[live]).max() <= 1e-5
+    assert np.all(gl[~live] == -np.inf) and np.all(to_f64(out32)[~live] == 0)
+    # and against the full oracle
+    ref, ref_lse = oracle_out(w)
+    assert np.abs(to_f64(out32) - ref).max() <= 1e-5 * 10
+    assert np.abs(gl[live] - ref_lse[live]).max() <= 1e-4
+
+
+def test_single_partition_merge_equals_partial(pkv):
+    w = small(2, batch=3, lengths=("uniform", 5, 200))
+    d = DeviceWorkload(w)
+    P = 256   # >= every length: one partition per row
+    po, pl = pkv.paged_decode_attention_partial(d.q, d.k_pool, d.v_pool, d.page_table,
+                                                d.context_lens, P, d.scale)
+    out = pkv.lse_merge(po, pl, d.context_lens, P, w.cfg.page_size, w.page_table.shape[1],
+                        out=torch.empty(w.q.shape, dtype=torch.float32, device="cuda"))
+    torch.cuda.synchronize()
+    assert np.abs(to_f64(out) - po[:, :, 0].double().cpu().numpy()).max() <= 1e-6
+
+
+# ----------------------------------------------------------------------------------------------
+# bit-exact page-table handling
+# ----------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("PS", [16, 32])
+def test_address_probe_every_slot_bit_exact(pkv, PS):
+    """One token scores 0 and every other scores <= -1e4, so the output is exactly that
+    token's V row: sweeping the token over every slot of every page proves the mapping."""
+    import dataclasses
+    cfg = dataclasses.replace(W.config(2), name="probe", batch=1, num_q_heads=4, num_kv_heads=2,
+                              head_dim=128, page_size=PS, lengths=("fixed", 3 * PS + 5),
+                              pool_pages=12)
+    w = W.make_workload(cfg)
+    L = int(w.context_lens[0])
+    bf = lambda x: np.uint16(np.float32(x).view(np.uint32) >> 16)
+    q = np.zeros_like(w.q)
+    q[0, :, 0] = bf(1.0)                     # every head: q = e0
+    T = 16 if PS == 16 else L                # sweep all slots for PS 16, every 3rd otherwise
+    d = DeviceWorkload(w)
+    d.q.copy_(to_device(q, "bf16"))
+    for t_star in range(L) if PS == 16 else range(0, L, 3):
+        kp = w.k_pool.copy()
+        for t in range(L):
+            page, slot = w.page_table[0, t // PS], t % PS
+            kp[page, slot, :, :] = 0
+            kp[page, slot, :, 0] = bf(0.0 if t == t_star else -30000.0)
+        d.k_pool.copy_(to_device(kp, "bf16"))
+        out = run_single(pkv, d)
+        out_s = run_split(pkv, d, PS)
+        got = to_numpy_storage(out, "bf16")
+        got_s = to_numpy_storage(out_s, "bf16")
+        page, slot = w.page_table[0, t_star // PS], t_star % PS
+        for h in range(4):
+            want = w.v_pool[page, slot, h // 2]
+            assert np.array_equal(got[0, h], want), (t_star, h)
+            assert np.array_equal(got_s[0, h], want), (t_star, h)
+    assert T > 0
+
+
+def test_single_token_context_returns_value_row(pkv):
+    w = small(2, batch=4, lengths=("fixed", 1))
+    d = DeviceWorkload(w)
+    out = to_numpy_storage(run_single(pkv, d), "bf16")
+    G = w.cfg.group
+    for b in range(4):
+        page = w.page_table[b, 0]
+        for h in range(w.cfg.num_q_heads):
+            assert np.array_equal(out[b, h], w.v_pool[page, 0, h // G])
+
+
+@pytest.mark.parametrize("path", ["single", "split"])
+def test_bitwise_invariance_relabel_poison_batch(pkv, path):
+    cfg = W.config(2).scaled(batch=6, lengths=("uniform", 1, 700))
+    w = W.make_workload(cfg)
+    run = (lambda d: run_single(pkv, d)) if path == "single" else (lambda d: run_split(pkv, d, 128))
+    base = to_numpy_storage(run(DeviceWorkload(w)), "bf16")
+    again = to_numpy_storage(run(DeviceWorkload(w)), "bf16")
+    assert np.array_equal(base, again), "run-to-run"
+    rel = to_numpy_storage(run(DeviceWorkload(W.relabel_pages(w, 77))), "bf16")
+    assert np.array_equal(base, rel), "page relabelling"
+    bad = W.make_workload(cfg, poison=True)
+    pois = to_numpy_storage(run(DeviceWorkload(bad)), "bf16")
+    assert np.array_equal(base, pois), "poisoned pages / tails / table entries"
+    rows = [4, 1]
+    sub = to_numpy_storage(run(DeviceWorkload(W.subset_rows(w, rows))), "bf16")
+    assert np.array_equal(base[rows], sub), "batch composition"
+
+
+def test_shared_prefix_bitwise_equals_unshared(pkv):
+    w = small(3, batch=5, lengths=("prefix", 128, 1, 90))
+    u = W.unshare_prefix(w)
+    a = to_numpy_storage(run_single(pkv, DeviceWorkload(w)), "f16")
+    b = to_numpy_storage(run_single(pkv, DeviceWorkload(u)), "f16")
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+    a = to_numpy_storage(run_split(pkv, DeviceWorkload(w), 64), "f16")
+    b = to_numpy_storage(run_split(pkv, DeviceWorkload(u), 64), "f16")
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+
+
+def test_empty_rows_and_padding(pkv):
+    w = small(2, batch=5, lengths=("uniform", 10, 200))
+    w = W.make_workload(w.cfg, pad_rows=[0, 3])
+    d = DeviceWorkload(w)
+    ref, _ = oracle_out(w)
+    for out in (run_single(pkv, d), run_split(pkv, d, 64)):
+        got = to_f64(out)
+        assert np.all(got[[0, 3]] == 0)
+        assert_parity(got, ref, "bf16", "padding rows")
+
+
+# ----------------------------------------------------------------------------------------------
+# append
+# ----------------------------------------------------------------------------------------------
+
+def test_append_raw_bytes_and_idempotence(pkv):
+    w = small(4, batch=9, lengths=("loguniform", 1, 300))
+    w = W.make_workload(w.cfg, pad_rows=[3])
+    d = DeviceWorkload(w)
+    pkv.paged_kv_append(d.k_new, d.v_new, d.k_pool, d.v_pool, d.page_table, d.append_lens)
+    kp, vp = O.paged_kv_append(w.k_pool, w.v_pool, w.k_new, w.v_new, w.page_table, w.append_lens)
+    gk = to_numpy_storage(d.k_pool, "bf16")
+    gv = to_numpy_storage(d.v_pool, "bf16")
+    assert np.array_equal(gk, kp) and np.array_equal(gv, vp)
+    pkv.paged_kv_append(d.k_new, d.v_new, d.k_pool, d.v_pool, d.page_table, d.append_lens)
+    assert np.array_equal(to_numpy_storage(d.k_pool, "bf16"), kp)
+    assert np.array_equal(to_numpy_storage(d.v_pool, "bf16"), vp)
+
+
+@pytest.mark.parametrize("dtype,D,Hkv", [("f32", 64, 2), ("f16", 128, 8), ("bf16", 64, 1)])
+def test_append_dtypes(pkv, dtype, D, Hkv):
+    import dataclasses
+    cfg = dataclasses.replace(W.config(4), name="append-" + dtype, batch=6, num_q_heads=Hkv,
+                              num_kv_heads=Hkv, head_dim=D, dtype=dtype, page_size=16,
+                              lengths=("uniform", 0, 100))
+    w = W.make_workload(cfg)
+    d = DeviceWorkload(w)
+    pkv.paged_kv_append(d.k_new, d.v_new, d.k_pool, d.v_pool, d.page_table, d.append_lens)
+    kp, vp = O.paged_kv_append(w.k_pool, w.v_pool, w.k_new, w.v_new, w.page_table, w.append_lens)
+    assert np.array_equal(to_numpy_storage(d.k_pool, dtype).view(np.uint8), kp.view(np.uint8))
+    assert np.array_equal(to_numpy_storage(d.v_pool, dtype).view(np.uint8), vp.view(np.uint8))
+
+
+# ----------------------------------------------------------------------------------------------
+# metadata validation
+# ----------------------------------------------------------------------------------------------
+
+def test_validate_metadata_matches_oracle(pkv):
+    w = small(4, batch=6, lengths=("uniform", 5, 200))
+    NP, PS = w.k_pool.shape[:2]
+    cases = []
+    cases.append((w.page_table.copy(), w.append_lens.copy()))
+    t = w.page_table.copy(); t[2, 0] = NP; cases.append((t, w.append_lens.copy()))
+    t = w.page_table.copy(); t[1, 0] = -7; cases.append((t, w.append_lens.copy()))
+    lens = w.append_lens.copy(); lens[4] = t.shape[1] * PS + 3; cases.append((w.page_table.copy(), lens))
+    t = w.page_table.copy(); t[0, int(w.append_lens[0]) // PS] = t[5, 0]; cases.append((t, w.append_lens.copy()))
+    for i, (t, lens) in enumerate(cases):
+        want = O.validate_metadata(t, lens, NP, PS, 1, True)
+        got = pkv.validate_metadata(torch.from_numpy(t).cuda(), torch.from_numpy(lens).cuda(),
+                                    NP, PS, extra_tokens=1, check_append_unique=True)
+        assert got == want, (i, got, want)
+        want0 = O.validate_metadata(t, lens, NP, PS, 1, False)
+        got0 = pkv.validate_metadata(torch.from_numpy(t).cuda(), torch.from_numpy(lens).cuda(),
+                                     NP, PS, extra_tokens=1, check_append_unique=False)
+        assert got0 == want0, (i, got0, want0)
+    assert [O.validate_metadata(t, l, NP, PS, 1, True) for t, l in cases] == [0, 1, 1, 2, 4]
+
+
+# ----------------------------------------------------------------------------------------------
+# host-side rejection leaves device state untouched
+# ----------------------------------------------------------------------------------------------
+
+def test_rejected_call_then_valid_call(pkv):
+    w = small(2, batch=3, lengths=("uniform", 10, 100))
+    d = DeviceWorkload(w)
+    out = run_single(pkv, d)
+    first = to_numpy_storage(out, "bf16").copy()
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.paged_decode_attention(d.q, d.k_pool, d.v_pool, d.page_table, d.context_lens,
+                                   float("inf"), out=out)
+    assert e.value.code == -1
+    assert np.array_equal(to_numpy_storage(out, "bf16"), first)
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.paged_decode_attention_partial(d.q, d.k_pool, d.v_pool, d.page_table, d.context_lens,
+                                           24, d.scale)
+    assert e.value.code == -1
+    out2 = run_single(pkv, d)
+    assert np.array_equal(to_numpy_storage(out2, "bf16"), first)
