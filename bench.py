@@ -1,0 +1,315 @@
+"""Decode-step benchmark for paged decode attention on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+
+One step is one decode step of the whole path over the Llama-3-8B-shaped batch (64 sequences,
+32 query heads, 8 KV heads, head_dim 128, page_size 16, bf16, contexts uniform in [512, 4096]):
+  1. paged KV append of each sequence's new token at position L - 1;
+  2. split-KV partial attention over the L tokens (partitions of 512 tokens);
+  3. log-sum-exp merge into the bf16 output.
+Inputs are seeded synthetic data, resident in HBM before timing starts.  The pools rotate over
+several replicas so that no step finds the previous step's KV in the 256 MB Infinity Cache.
+
+Prints one JSON line: whole-step throughput in algorithmic GB/s (KV rows of every live token once,
+q, out, page-table entries, append rows and split partials), decode tokens/s (= sequences per
+step / step time), the roofline of the dominant kernel measured with HIP events on the launch
+stream, and the fp64 CPU oracle's rate on the host for reference.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attention HBM GB/s (% of peak) + decode tokens/sec, 1 MI355X"
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[1])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=2, help="workload index (default: 2)")
+    ap.add_argument("--path", choices=["step", "split", "single"], default="step")
+    ap.add_argument("--partition-tokens", type=int, default=None)
+    ap.add_argument("--replicas", type=int, default=None,
+                    help="pool replicas rotated per step (default: enough for >= 2 GB)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="minimum host time spent timing the CPU oracle (0 disables it)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain device copy of known size (counter calibration)")
+    return ap.parse_args()
+
+
+def step_bytes(w, partition_tokens, path):
+    """Algorithmic bytes of one step and of its dominant kernel launch."""
+    import numpy as np
+    cfg = w.cfg
+    e = cfg.elem_bytes
+    B, Hq, D, Hkv, PS = cfg.batch, cfg.num_q_heads, cfg.head_dim, cfg.num_kv_heads, cfg.page_size
+    L = np.maximum(w.context_lens.astype(np.int64), 0)
+    kv = int(L.sum()) * 2 * Hkv * D * e
+    q = out = B * Hq * D * e
+    table = int((-(-L // PS)).sum()) * 4 + B * 4
+    append = 2 * (2 * B * Hkv * D * e) + B * 4 + B * 4
+    if path == "split":
+        nparts = -(-L // partition_tokens)
+        partials = int(nparts.sum()) * Hq * (D + 1) * 4
+        kernel = kv + q + table + partials            # partial-attention launch
+        step = kv + q + out + table + append + 2 * partials + B * 4
+    elif path == "step":
+        # One piece partial per (workgroup range, sequence) crossing; bounded by groups + B.
+        pieces = partition_tokens
+        partials = pieces * Hq * (D + 1) * 4
+        kernel = kv + q + table + append + partials
+        step = kernel + partials + out + B * 4
+    else:
+        kernel = kv + q + out + table
+        step = kernel + append
+    return dict(kv=kv, step=step, kernel=kernel)
+
+
+def copy_calibration(nbytes=2 << 30, reps=20):
+    import torch
+    a = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").normal_()
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / reps
+    gbs = 2 * nbytes / (ms * 1e-3) / 1e9
+    log(f"plain copy: {nbytes / 2**30:.1f} GiB read + write, {ms:.3f} ms/launch, {gbs:.0f} GB/s")
+    return {"bytes_read": nbytes, "bytes_written": nbytes, "ms": ms, "gbs": gbs}
+
+
+def cpu_baseline(w, extra_new, seconds):
+    """Time the fp64 oracle (append + attention) on the host over a bounded sample."""
+    import numpy as np
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    rows = list(range(w.cfg.batch))
+    k_new, v_new, append_lens = extra_new
+
+    def one():
+        kp, vp = O.paged_kv_append(w.k_pool, w.v_pool, k_new, v_new, w.page_table, append_lens)
+        O.paged_decode_attention(w.q, kp, vp, w.page_table, w.context_lens, w.scale, w.dtype)
+
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    if ctx:
+        ctx.__enter__()
+    try:
+        n = 0
+        t0 = time.perf_counter()
+        while True:
+            one()
+            n += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        dt = (time.perf_counter() - t0) / n
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    kv = int(np.maximum(w.context_lens.astype(np.int64), 0).sum()) * w.kv_bytes_per_token()
+    return {"value": round(kv / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "tokens_per_s": round(len(rows) / dt, 3), "s_per_step": round(dt, 4),
+            "sample": (f"whole {w.cfg.name} step (append + attention, all {len(rows)} rows), "
+                       f"{n} repetition(s), float64 NumPy, BLAS limited to 1 thread"),
+            "cpu": platform.processor() or platform.machine()}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}): "
+              "this build has no multi-GPU path; run with --gpus 1.", flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_203_amd as pkv
+    import workloads as W
+    from workloads.generate import STREAM_KNEW, STREAM_VNEW, fill_normal
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    if args.copy_calibration:
+        print(json.dumps({"copy_calibration": copy_calibration()}), flush=True)
+        return
+
+    cfg = W.config(args.config)
+    t_gen = time.perf_counter()
+    w = W.make_workload(cfg)
+    B, Hq, Hkv, D, PS = cfg.batch, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.page_size
+    if cfg.append:
+        k_new, v_new, append_lens = w.k_new, w.v_new, w.append_lens
+    else:
+        # The decode step writes its own token: the new row lands at position L - 1, so that
+        # attention covers exactly the workload's context lengths.
+        k_new = fill_normal((B, Hkv, D), cfg.dtype, w.seed, STREAM_KNEW)
+        v_new = fill_normal((B, Hkv, D), cfg.dtype, w.seed, STREAM_VNEW)
+        append_lens = (w.context_lens - 1).astype(np.int32)
+    P = args.partition_tokens or cfg.partition_tokens or 512
+    log(f"workload {cfg.name}: generated in {time.perf_counter() - t_gen:.1f}s, "
+        f"{w.logical_tokens()} live tokens, pool {w.k_pool.shape}")
+
+    def to_device(arr, dtype, device):
+        a = np.ascontiguousarray(arr)
+        if dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+        return torch.from_numpy(a).to(device)
+
+    dev = torch.device("cuda:0")
+    q = to_device(w.q, cfg.dtype, dev)
+    table = torch.from_numpy(w.page_table).to(dev)
+    lens = torch.from_numpy(w.context_lens).to(dev)
+    alens = torch.from_numpy(append_lens).to(dev)
+    kn = to_device(k_new, cfg.dtype, dev)
+    vn = to_device(v_new, cfg.dtype, dev)
+    k0 = to_device(w.k_pool, cfg.dtype, dev)
+    v0 = to_device(w.v_pool, cfg.dtype, dev)
+    pool_bytes = 2 * k0.numel() * k0.element_size()
+    R = args.replicas or max(1, math.ceil((2 << 30) / pool_bytes))
+    pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(R - 1)]
+    out = torch.empty_like(q)
+    maxp = pkv.partitions_needed(PS, w.page_table.shape[1], P)
+    po = torch.empty((B, Hq, maxp, D), dtype=torch.float32, device=dev)
+    pl = torch.empty((B, Hq, maxp), dtype=torch.float32, device=dev)
+    scale = float(w.scale)
+    stream = torch.cuda.current_stream(dev)
+
+    ws = None
+    if args.path == "step":
+        ws = torch.zeros(pkv.decode_step_workspace_bytes(q, k0, table), dtype=torch.uint8, device=dev)
+
+    def step(i, ev=None):
+        kp, vp = pools[i % R]
+        if args.path == "step":
+            if ev is not None:
+                ev[0].record(stream)
+            pkv.paged_decode_step(q, kp, vp, table, alens, scale, k_new=kn, v_new=vn, out=out,
+                                  workspace=ws)
+            if ev is not None:
+                ev[1].record(stream)
+            return
+        pkv.paged_kv_append(kn, vn, kp, vp, table, alens)
+        if ev is not None:
+            ev[0].record(stream)
+        if args.path == "split":
+            pkv.paged_decode_attention_partial(q, kp, vp, table, lens, P, scale, po, pl, maxp)
+            if ev is not None:
+                ev[1].record(stream)
+            pkv.lse_merge(po, pl, lens, P, PS, w.page_table.shape[1], out=out)
+        else:
+            pkv.paged_decode_attention(q, kp, vp, table, lens, scale, out)
+            if ev is not None:
+                ev[1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = [a.elapsed_time(b) for a, b in evs]
+
+    if args.path == "step":
+        # pieces written by the balanced split: one per (workgroup range, sequence) crossing
+        groups = torch.cuda.get_device_properties(0).multi_processor_count
+        nb = step_bytes(w, groups + B, "step")
+    else:
+        nb = step_bytes(w, P, args.path)
+    ms_step = wall * 1e3 / K
+    gbs = nb["step"] / (ms_step * 1e-3) / 1e9
+    k_avg = float(np.mean(kernel_ms))
+    k_gbs = nb["kernel"] / (k_avg * 1e-3) / 1e9
+    log(f"{K} steps in {wall * 1e3:.2f} ms: {ms_step * 1e3:.1f} us/step, {gbs:.0f} GB/s step, "
+        f"dominant kernel {k_avg * 1e3:.1f} us avg (p10 {np.percentile(kernel_ms, 10) * 1e3:.1f}, "
+        f"p90 {np.percentile(kernel_ms, 90) * 1e3:.1f}), {k_gbs:.0f} GB/s")
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        log(f"timing the CPU oracle for >= {args.cpu_seconds:.0f}s ...")
+        cpu = cpu_baseline(w, (k_new, v_new, append_lens), args.cpu_seconds)
+        log(f"CPU oracle: {cpu['s_per_step']:.3f} s/step, {cpu['value']} GB/s")
+
+    kernel_name = {"split": "decode_kernel (split-KV partial attention)",
+                   "single": "decode_kernel (single pass)",
+                   "step": "pkv_paged_decode_step (balanced attention with fused append + merge)"}[args.path]
+    line = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": cfg.name,
+            "description": {"split": "append + split-KV paged decode attention + LSE merge",
+                            "single": "append + single-pass paged decode attention",
+                            "step": "one decode step: append fused into balanced split-KV attention, then LSE merge"}[args.path],
+            "batch": B, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D, "page_size": PS,
+            "context_lens": list(cfg.lengths), "seed": w.seed, "live_tokens": w.logical_tokens(),
+            "partition_tokens": P if args.path == "split" else None, "path": args.path,
+            "pool_replicas": R,
+            "step_bytes": nb["step"], "kv_bytes": nb["kv"],
+        },
+        "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "decode_tokens_per_s": round(B / (ms_step * 1e-3), 1),
+        "roofline": {
+            "kernel": kernel_name,
+            "bound": "hbm",
+            "achieved": round(k_gbs, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(k_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "bytes_per_launch": nb["kernel"],
+            "avg_launch_us": round(k_avg * 1e3, 3),
+        },
+        "cpu_baseline": cpu,
+        "device": torch.cuda.get_device_name(0),
+        "torch": torch.__version__,
+        "lib": pkv.version(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

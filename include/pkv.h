@@ -136,6 +136,39 @@ int pkv_paged_kv_append(const void* k_new, const void* v_new, void* k_pool, void
                         const int32_t* page_table, const int32_t* context_lens,
                         const pkv_shape* shape, void* stream);
 
+/* One whole decode step in one call, with the work split evenly over the GPU.
+ *
+ * With k_new and v_new non-NULL, every sequence's new K and V rows are first written into the
+ * pools at position context_lens[b] (exactly as pkv_paged_kv_append), and attention then covers
+ * context_lens[b] + 1 tokens.  With both NULL, the pools are only read and attention covers
+ * context_lens[b] tokens.  out / lse_out are as for pkv_lse_merge (lse_out may be NULL); rows
+ * with no tokens get out = 0, lse = -inf.
+ *
+ * The batch's tiles of 16 tokens are cut into equal contiguous ranges, one per workgroup and as
+ * many workgroups as the GPU holds at once, so every compute unit gets the same share whatever
+ * the mix of lengths; a range can hold pieces of several sequences, and the pieces of a sequence
+ * are combined with the log-sum-exp rule (the flash-decoding split; CacheIR page, "Current
+ * Capabilities": persistent multi-batch page-table decode).  Results agree with
+ * pkv_paged_decode_attention to rounding and are deterministic for a given batch, but unlike the
+ * fixed-partition calls their last bits can depend on the other sequences (the split points do).
+ *
+ * It is one launch: the workgroup that finishes the last piece of a sequence merges it, found
+ * through per-sequence arrival counters kept in the workspace.
+ *
+ * workspace: caller-owned device memory of at least pkv_decode_step_workspace_bytes(shape)
+ * bytes (queried on the same device), 16-byte aligned, zero-filled before its first use; every
+ * call leaves its counters at zero again, so it can be reused without clearing.  Calls that
+ * share a workspace must not run concurrently.  Supports batch <= 4096 (else
+ * PKV_EUNSUPPORTED). */
+int pkv_paged_decode_step(const void* q, const void* k_new, const void* v_new, void* k_pool,
+                          void* v_pool, const int32_t* page_table, const int32_t* context_lens,
+                          float scale, void* workspace, size_t workspace_bytes, void* out,
+                          float* lse_out, const pkv_shape* shape, void* stream);
+
+/* Workspace bytes pkv_paged_decode_step needs on the current device (0 on a bad shape or when
+ * no device is available). */
+size_t pkv_decode_step_workspace_bytes(const pkv_shape* shape);
+
 /* Device-side check of the metadata preconditions.  Rows with L = context_lens[b] +
  * extra_tokens > 0 are live and use n = ceil(L / PS) table entries.  Writes one int32 status
  * word to device_status (stream-ordered; read it after the stream completes):

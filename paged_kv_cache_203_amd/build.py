@@ -1,6 +1,9 @@
 """Build libpkv.so in-tree for gfx950 with hipcc.
 
-    python -m paged_kv_cache_203_amd.build          # compiles every source, always
+    python paged_kv_cache_203_amd/build.py          # compiles every source, always
+
+This file is self-contained and is run by path: importing the package would load the library
+it is about to rebuild.
 
 The HIP sources are compiled with packed-fp32 instruction selection disabled; the host-only
 argument checker is compiled with g++.  Objects go to ``_build/`` and the library to

@@ -26,6 +26,25 @@ int log2_exact(int32_t x) {
 
 int group_pad(int g) { return g <= 4 ? 4 : (g <= 8 ? 8 : 16); }
 
+// Largest divisor of hkv that also divides the decode workgroup's wave count.
+int heads_per_workgroup(int hkv) {
+  const int waves = pkv::decode_waves();
+  int best = 1;
+  for (int h = 1; h <= waves; ++h)
+    if (hkv % h == 0 && waves % h == 0) best = h;
+  return best;
+}
+
+// Workgroup ranges of the balanced decode step on the current device: one 8-wave workgroup per
+// compute unit, shared among the KV-head groups.  0 when no device is available.
+int64_t step_groups(const pkv_shape& s) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  const int nhg = s.num_kv_heads / heads_per_workgroup(s.num_kv_heads);
+  return cus / nhg > 0 ? cus / nhg : 1;
+}
+
 int launch_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return PKV_OK;
   return set_error(PKV_ELAUNCH, std::string(what) + ": " + hipGetErrorString(e));
@@ -81,6 +100,7 @@ int pkv_paged_decode_attention(const void* q, const void* k_pool, const void* v_
   p.out = out;
   p.partition_tokens = p.capacity;
   p.max_partitions = 1;
+  p.heads_per_wg = 1;   // one KV head per workgroup: its waves share the whole sequence
   (void)hipGetLastError();
   return launch_status(pkv::launch_decode(p, shape->dtype, shape->head_dim, group_pad(p.group),
                                           false, static_cast<hipStream_t>(stream)),
@@ -104,10 +124,54 @@ int pkv_paged_decode_attention_partial(const void* q, const void* k_pool, const 
   p.partial_lse = partial_lse;
   p.partition_tokens = partition_tokens;
   p.max_partitions = max_partitions;
+  p.heads_per_wg = heads_per_workgroup(p.hkv);   // whole pages per workgroup
   (void)hipGetLastError();
   return launch_status(pkv::launch_decode(p, shape->dtype, shape->head_dim, group_pad(p.group),
                                           true, static_cast<hipStream_t>(stream)),
                        "pkv_paged_decode_attention_partial");
+}
+
+size_t pkv_decode_step_workspace_bytes(const pkv_shape* shape) {
+  std::string msg;
+  if (pkv::check_shape(shape, msg) != PKV_OK) return 0;
+  const int64_t groups = step_groups(*shape);
+  if (groups == 0) return 0;
+  return size_t(pkv::step_workspace(*shape, groups, heads_per_workgroup(shape->num_kv_heads)).bytes);
+}
+
+int pkv_paged_decode_step(const void* q, const void* k_new, const void* v_new, void* k_pool,
+                          void* v_pool, const int32_t* page_table, const int32_t* context_lens,
+                          float scale, void* workspace, size_t workspace_bytes, void* out,
+                          float* lse_out, const pkv_shape* shape, void* stream) {
+  std::string msg;
+  int rc = pkv::check_shape(shape, msg);
+  if (rc) return set_error(rc, "pkv_paged_decode_step: " + msg);
+  const int64_t groups = shape->batch ? step_groups(*shape) : 1;
+  const pkv::StepWorkspace ws =
+      pkv::step_workspace(*shape, groups ? groups : 1, heads_per_workgroup(shape->num_kv_heads));
+  rc = pkv::check_step(q, k_new, v_new, k_pool, v_pool, page_table, context_lens, scale, workspace,
+                       workspace_bytes, groups ? ws.bytes : 0, out, lse_out, shape, msg);
+  if (rc) return set_error(rc, "pkv_paged_decode_step: " + msg);
+  if (shape->batch == 0) return PKV_OK;
+  pkv::StepParams p{};
+  p.a = decode_params(q, k_pool, v_pool, page_table, context_lens, scale, *shape);
+  p.a.heads_per_wg = heads_per_workgroup(p.a.hkv);
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.k_pool_w = k_pool;
+  p.v_pool_w = v_pool;
+  char* w = static_cast<char*>(workspace);
+  p.ws_out = reinterpret_cast<float*>(w + ws.out_off);
+  p.ws_lse = reinterpret_cast<float*>(w + ws.lse_off);
+  p.ws_count = reinterpret_cast<int32_t*>(w + ws.count_off);
+  p.out = out;
+  p.lse_out = lse_out;
+  p.groups = int32_t(groups);
+  p.append = k_new ? 1 : 0;
+  (void)hipGetLastError();
+  return launch_status(pkv::launch_step(p, shape->dtype, shape->head_dim, group_pad(p.a.group),
+                                        static_cast<hipStream_t>(stream)),
+                       "pkv_paged_decode_step");
 }
 
 int pkv_lse_merge(const float* partial_out, const float* partial_lse,

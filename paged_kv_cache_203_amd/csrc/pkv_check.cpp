@@ -198,6 +198,65 @@ int check_append(const void* k_new, const void* v_new, const void* k_pool, const
   return PKV_OK;
 }
 
+StepWorkspace step_workspace(const pkv_shape& s, int64_t groups, int heads_per_wg) {
+  auto up = [](uint64_t x) { return (x + 255) & ~uint64_t(255); };
+  const uint64_t pieces = uint64_t(groups) + uint64_t(s.batch);
+  const uint64_t head_groups = uint64_t(s.num_kv_heads / heads_per_wg);
+  StepWorkspace w;
+  w.out_off = 0;
+  w.lse_off = up(pieces * s.num_q_heads * s.head_dim * 4);
+  w.count_off = w.lse_off + up(pieces * s.num_q_heads * 4);
+  w.bytes = w.count_off + up(uint64_t(s.batch) * head_groups * 4);
+  return w;
+}
+
+int check_step(const void* q, const void* k_new, const void* v_new, const void* k_pool,
+               const void* v_pool, const int32_t* page_table, const int32_t* context_lens,
+               float scale, const void* workspace, size_t workspace_bytes, uint64_t needed,
+               const void* out, const float* lse_out, const pkv_shape* s, std::string& msg) {
+  int rc = check_shape(s, msg);
+  if (rc) return rc;
+  if (s->batch > 4096) return fail(msg, PKV_EUNSUPPORTED, "batch must be <= 4096 for the decode step");
+  if (s->batch == 0) return PKV_OK;
+  rc = check_attention_inputs(q, k_pool, v_pool, page_table, context_lens, scale, msg);
+  if (rc) return rc;
+  if ((k_new == nullptr) != (v_new == nullptr))
+    return fail(msg, PKV_EINVAL, "k_new and v_new must both be given or both be NULL");
+  if (k_new && (!aligned(k_new, 16) || !aligned(v_new, 16)))
+    return fail(msg, PKV_EUNSUPPORTED, "k_new and v_new must be 16-byte aligned");
+  if (!out) return fail(msg, PKV_EINVAL, "out must be non-NULL");
+  if (!aligned(out, 16)) return fail(msg, PKV_EUNSUPPORTED, "out must be 16-byte aligned");
+  if (lse_out && !aligned(lse_out, 4)) return fail(msg, PKV_EINVAL, "lse_out must be 4-byte aligned");
+  if (!workspace) return fail(msg, PKV_EINVAL, "workspace must be non-NULL");
+  if (!aligned(workspace, 16)) return fail(msg, PKV_EINVAL, "workspace must be 16-byte aligned");
+  const Extents x = extents(*s);
+  const uint64_t lo = uint64_t(s->batch) * s->num_q_heads * 4;
+  const void* ins[7] = {q, k_pool, v_pool, page_table, context_lens, k_new, v_new};
+  const uint64_t ins_n[7] = {x.q, x.pool, x.pool, x.table, x.lens, x.new_rows, x.new_rows};
+  for (int i = 0; i < 7; ++i) {
+    if (overlaps(out, x.out, ins[i], ins_n[i])) return fail(msg, PKV_EINVAL, "out overlaps an input");
+    if (overlaps(workspace, workspace_bytes, ins[i], ins_n[i]))
+      return fail(msg, PKV_EINVAL, "workspace overlaps an input");
+    if (lse_out && overlaps(lse_out, lo, ins[i], ins_n[i]))
+      return fail(msg, PKV_EINVAL, "lse_out overlaps an input");
+  }
+  if (overlaps(out, x.out, workspace, workspace_bytes) || (lse_out && overlaps(lse_out, lo, workspace, workspace_bytes)) ||
+      (lse_out && overlaps(lse_out, lo, out, x.out)))
+    return fail(msg, PKV_EINVAL, "out, lse_out and workspace must not overlap");
+  if (k_new) {
+    if (overlaps(k_pool, x.pool, v_pool, x.pool)) return fail(msg, PKV_EINVAL, "k_pool overlaps v_pool");
+    const void* rd[4] = {k_new, v_new, page_table, context_lens};
+    const uint64_t rd_n[4] = {x.new_rows, x.new_rows, x.table, x.lens};
+    for (int i = 0; i < 4; ++i)
+      if (overlaps(k_pool, x.pool, rd[i], rd_n[i]) || overlaps(v_pool, x.pool, rd[i], rd_n[i]))
+        return fail(msg, PKV_EINVAL, "a pool overlaps an input of the append");
+  }
+  if (needed == 0) return fail(msg, PKV_ELAUNCH, "no device available to size the workspace");
+  if (workspace_bytes < needed)
+    return fail(msg, PKV_EWORKSPACE, "workspace smaller than pkv_decode_step_workspace_bytes()");
+  return PKV_OK;
+}
+
 int check_validate(const int32_t* page_table, const int32_t* context_lens, int32_t extra_tokens,
                    const int32_t* device_status, const pkv_shape* s, std::string& msg) {
   int rc = check_shape(s, msg);

@@ -46,6 +46,19 @@ int check_append(const void* k_new, const void* v_new, const void* k_pool, const
                  const int32_t* page_table, const int32_t* context_lens, const pkv_shape* s,
                  std::string& msg);
 
+// Workspace layout of the balanced decode step for `groups` workgroup ranges (all offsets
+// 256-byte aligned): piece outputs, piece log-sum-exps, arrival counters (one per sequence and
+// group of heads_per_wg KV heads).
+struct StepWorkspace {
+  uint64_t out_off, lse_off, count_off, bytes;
+};
+StepWorkspace step_workspace(const pkv_shape& s, int64_t groups, int heads_per_wg);
+
+int check_step(const void* q, const void* k_new, const void* v_new, const void* k_pool,
+               const void* v_pool, const int32_t* page_table, const int32_t* context_lens,
+               float scale, const void* workspace, size_t workspace_bytes, uint64_t needed,
+               const void* out, const float* lse_out, const pkv_shape* s, std::string& msg);
+
 int check_validate(const int32_t* page_table, const int32_t* context_lens, int32_t extra_tokens,
                    const int32_t* device_status, const pkv_shape* s, std::string& msg);
 

@@ -1,0 +1,182 @@
+// Device-side primitives shared by the libpkv kernels (gfx950): element conversions, streaming
+// and direct-to-LDS loads, explicit wait counters, cross-row lane exchanges.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+namespace dev {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2;
+constexpr int kTile = 16;
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLog2e = 1.44269504088896340736f;
+
+template <int DT>
+constexpr int elem_size() { return DT == DT_F32 ? 4 : 2; }
+
+__device__ inline float neg_inf() { return -__builtin_inff(); }
+__device__ inline float qnan() { return __builtin_nanf(""); }
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Two packed 16-bit elements -> two floats (exact).
+template <int DT>
+__device__ inline void unpack2(uint32_t w, float& lo, float& hi) {
+  if constexpr (DT == DT_BF16) {
+    lo = __uint_as_float(w << 16);
+    hi = __uint_as_float(w & 0xffff0000u);
+  } else {
+    lo = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w & 0xffffu)));
+    hi = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w >> 16)));
+  }
+}
+
+// float -> element bits, round to nearest even.
+template <int DT>
+__device__ inline void store_elem(void* base, int64_t idx, float x) {
+  if constexpr (DT == DT_F32) {
+    static_cast<float*>(base)[idx] = x;
+  } else if constexpr (DT == DT_BF16) {
+    uint32_t u = __float_as_uint(x);
+    uint16_t r;
+    if ((u & 0x7fffffffu) > 0x7f800000u) {
+      r = 0x7fc0;  // NaN
+    } else {
+      r = static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+    }
+    static_cast<uint16_t*>(base)[idx] = r;
+  } else {
+    static_cast<_Float16*>(base)[idx] = static_cast<_Float16>(x);
+  }
+}
+
+// Global-address-space byte pointer (loads through it are global_load, never flat_load).
+typedef const __attribute__((address_space(1))) char* gptr;
+typedef const __attribute__((address_space(1))) u32x4* gptr_u32x4;
+typedef const __attribute__((address_space(1))) u32x2* gptr_u32x2;
+
+// Generic pointer known to address global memory -> global address space.
+__device__ inline gptr to_gptr(const char* p) { return (gptr)p; }
+
+// Streaming loads of K/V rows: each byte is used once, so they are marked non-temporal (the
+// nt bit), which keeps the caches free for the rest of the stream.
+__device__ inline u32x4 stream_load16(gptr p) {
+  return __builtin_nontemporal_load(reinterpret_cast<gptr_u32x4>(p));
+}
+
+// N 32-bit words from 4N contiguous bytes (N in {2, 4, 8}).
+template <int N>
+__device__ inline void load_words(gptr p, uint32_t (&w)[N]) {
+  if constexpr (N == 2) {
+    const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<gptr_u32x2>(p));
+    w[0] = v.x;
+    w[1] = v.y;
+  } else {
+#pragma unroll
+    for (int i = 0; i < N / 4; ++i) {
+      const u32x4 v = stream_load16(p + 16 * i);
+      w[4 * i + 0] = v.x;
+      w[4 * i + 1] = v.y;
+      w[4 * i + 2] = v.z;
+      w[4 * i + 3] = v.w;
+    }
+  }
+}
+
+// Cross-row exchanges on VALU (gfx950 permlane swaps): lane l sees lanes l ^ 16 / l ^ 32.
+// Both lanes of a pair combine the two values in the same order, so results are identical.
+__device__ inline void swap16(float x, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+__device__ inline void swap32(float x, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+__device__ inline float max_rows4(float x) {   // max over lanes {l, l^16, l^32, l^48}
+  float a, b;
+  swap16(x, a, b);
+  x = fmaxf(a, b);
+  swap32(x, a, b);
+  return fmaxf(a, b);
+}
+__device__ inline float sum_rows4(float x) {   // sum over lanes {l, l^16, l^32, l^48}
+  float a, b;
+  swap16(x, a, b);
+  x = a + b;
+  swap32(x, a, b);
+  return a + b;
+}
+
+// s_waitcnt that waits until at most `n` vector-memory loads of this wave are outstanding
+// (expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// 16-byte LDS read issued as inline assembly.  The K stages are filled by direct-to-LDS loads
+// whose completion this kernel tracks itself (explicit vmcnt waits), so these reads are kept
+// out of the compiler's conservative alias tracking.  The values may only be used after
+// lds_wait_all() has passed them through its wait.
+__device__ inline u32x4 lds_read16(uint32_t lds_addr) {
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(lds_addr));
+  return r;
+}
+
+// s_waitcnt lgkmcnt(0) that the compiler cannot schedule uses of `r` above: the registers are
+// operands of the waiting instruction.
+template <int N>
+__device__ inline void lds_wait_all(u32x4 (&r)[N]) {
+  static_assert(N == 2 || N == 4 || N == 8, "operand count");
+  if constexpr (N == 2) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r[0]), "+v"(r[1]));
+  } else if constexpr (N == 4) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]));
+  } else {
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]),
+                   "+v"(r[6]), "+v"(r[7]));
+  }
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes land at
+// lds_dst + 16 l (lds_dst is a wave-uniform LDS byte address).  Completion is tracked by vmcnt.
+template <int AUX>
+__device__ inline void dma16_to_lds(gptr src, uint32_t lds_dst) {
+  __builtin_amdgcn_global_load_lds(src, reinterpret_cast<__attribute__((address_space(3))) void*>(
+                                            static_cast<uintptr_t>(lds_dst)),
+                                   16, 0, AUX);
+}
+
+// Cache-policy bits of the K-row copies (non-temporal: streamed once).
+constexpr int kDmaPolicy = 2;
+
+// LDS byte address of a __shared__ object.
+__device__ inline uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)p));
+}
+
+// A wave-uniform global pointer, forced into scalar registers (SGPR base + VGPR offset loads).
+__device__ inline gptr uniform_gptr(const char* ptr) {
+  const uint64_t v = reinterpret_cast<uint64_t>(ptr);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<gptr>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+}  // namespace dev
+}  // namespace pkv

@@ -1,136 +1,361 @@
 // HIP kernels for paged decode attention on CDNA4 (gfx950).
 //
-// Work unit.  One workgroup of NW wavefronts handles one (sequence b, KV head, partition): the
-// G = Hq / Hkv query heads of a GQA group read each K/V row of that KV head once.  The unit's
-// tokens are cut into tiles of 16 (a tile never straddles a page, since page_size is a multiple
-// of 16); wave w takes tiles w, w + NW, w + 2 NW, ...  The order in which a token is reduced
-// depends only on its logical position and the partition size, never on physical page ids or
-// on the rest of the batch, so results are bitwise invariant under page relabelling, prefix
-// sharing and batch composition.
+// The hot loop (HeadPipe) streams one KV head of one sequence through one wavefront:
+//  * Tiles of 16 tokens; a tile never straddles a page (page_size is a multiple of 16), so its
+//    16 rows sit at one page-table entry: page_table[b][t0 / page_size], slot t0 % page_size.
+//    Page ids are fetched one per lane for 64 tiles at a time and broadcast with readlane.
+//  * K rows are copied global -> LDS with 16-byte direct-to-LDS loads, 16 lanes per row, so every
+//    load instruction reads whole rows.  In LDS, slice j of token t sits at j ^ (t & SWZ), which
+//    keeps the MFMA-layout reads below free of bank conflicts.
+//  * V rows are loaded into registers the same way (16 lanes per row), in the layout PV uses.
+//  * S^T (16 tokens x 16 head slots) = K_tile . Q^T on MFMA: the G query heads of the GQA group
+//    (zero-padded to 16 columns) share every K row read.
+//  * Online softmax in the MFMA output layout (lane l: tokens 4(l/16)..+3 of head l % 16), base 2.
+//  * p goes through a per-wave LDS slot to the PV layout; PV accumulates in float32 on VALU, so
+//    probabilities are never rounded to 16 bits.
+//  * DEPTH tiles are in flight per wave (K stages in LDS, V in registers), waited for with
+//    explicit vmcnt counts.
+// The order in which a token is reduced depends only on its logical position and on the token
+// range a wave is given, never on physical page ids, so results are bitwise invariant under
+// page relabelling and prefix sharing.
 //
-// Per tile (16 tokens):
-//  * page-table resolution: one scalar load of page_table[b][t0 / page_size] (prefetched one tile
-//    ahead); the tile's 16 slots are contiguous rows of that page.
-//  * QK: S^T (16 tokens x 16 head slots) = K_tile (16 x D) . Q^T (D x 16) on MFMA.  Lane l feeds
-//    token l % 16 and a 16-byte slice of its K row straight from a global load, so K needs no
-//    LDS staging; the G query heads (zero-padded to 16 columns) share every K read.
-//  * online softmax in the MFMA output layout: lane l holds tokens 4*(l/16)..+3 of head l % 16;
-//    the running max is kept per head (base-2 domain, exp2), the running sum per lane.
-//  * p hand-off: each wave writes its 16 x G probabilities to a private LDS slot and reads them
-//    back broadcast in the PV layout.
-//  * PV on VALU in float32: lane l owns D/16 contiguous dims of token 4r + l/16 in round r, so the
-//    V loads of a round are 4 whole rows (coalesced) and p stays exact float32 (no rounding of
-//    probabilities to 16 bits).
-// At the end the waves' (max, sum, accumulator) triples are merged in LDS in wave order.
+// Kernels:
+//  * decode_kernel: one workgroup per (sequence, partition, group of KV heads).  Partitions are
+//    fixed multiples of partition_tokens, so a sequence's bits never depend on the batch.
+//  * step_kernel: one whole decode step in one launch, with the work split evenly over the GPU —
+//    the batch's tiles are cut into one contiguous range per workgroup, and a range may cover
+//    pieces of several sequences.  The workgroup that holds a sequence's last tile first writes
+//    the appended token's K/V rows into the pool, then reads them back with that tile.  The
+//    last workgroup to finish a piece of a sequence merges the sequence's pieces.
+//  * merge kernels: log-sum-exp combination of partial results.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "pkv_device.h"
 #include "pkv_launch.h"
 
 namespace pkv {
 namespace {
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+using namespace dev;
 
-constexpr int DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2;
-constexpr int kTile = 16;
-constexpr float kLn2 = 0.69314718055994530942f;
-constexpr float kLog2e = 1.44269504088896340736f;
+// Tiles handled per wave between page-table refreshes: one page id per lane.
+constexpr int kChunk = 64;
 
-template <int DT>
-constexpr int elem_size() { return DT == DT_F32 ? 4 : 2; }
-
-__device__ inline float neg_inf() { return -__builtin_inff(); }
-__device__ inline float qnan() { return __builtin_nanf(""); }
-
-__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Two packed 16-bit elements -> two floats (exact).
-template <int DT>
-__device__ inline void unpack2(uint32_t w, float& lo, float& hi) {
-  if constexpr (DT == DT_BF16) {
-    lo = __uint_as_float(w << 16);
-    hi = __uint_as_float(w & 0xffff0000u);
-  } else {
-    lo = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w & 0xffffu)));
-    hi = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w >> 16)));
-  }
-}
-
-// float -> element bits, round to nearest even.
-template <int DT>
-__device__ inline void store_elem(void* base, int64_t idx, float x) {
-  if constexpr (DT == DT_F32) {
-    static_cast<float*>(base)[idx] = x;
-  } else if constexpr (DT == DT_BF16) {
-    uint32_t u = __float_as_uint(x);
-    uint16_t r;
-    if ((u & 0x7fffffffu) > 0x7f800000u) {
-      r = 0x7fc0;  // NaN
-    } else {
-      r = static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
-    }
-    static_cast<uint16_t*>(base)[idx] = r;
-  } else {
-    static_cast<_Float16*>(base)[idx] = static_cast<_Float16>(x);
-  }
-}
-
-// N 32-bit words from 4N contiguous bytes (N in {2, 4, 8}).
-template <int N>
-__device__ inline void load_words(const char* p, uint32_t (&w)[N]) {
-  if constexpr (N == 2) {
-    const u32x2 v = *reinterpret_cast<const u32x2*>(p);
-    w[0] = v.x;
-    w[1] = v.y;
-  } else {
-#pragma unroll
-    for (int i = 0; i < N / 4; ++i) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(p + 16 * i);
-      w[4 * i + 0] = v.x;
-      w[4 * i + 1] = v.y;
-      w[4 * i + 2] = v.z;
-      w[4 * i + 3] = v.w;
-    }
-  }
-}
-
-// Registers of one tile for one lane.
-template <int NKL, int VW>
-struct TileRegs {
-  u32x4 k[NKL];          // K: 16-byte slices of token (lane % 16)
-  uint32_t v[4][VW];     // V: round r holds dims of token 4r + lane / 16
+// Geometry of one tile of one KV head.
+template <int DT, int D>
+struct TileGeo {
+  static constexpr int E = elem_size<DT>();
+  static constexpr int RB = D * E;              // bytes of one row (one token, one KV head)
+  static constexpr int SPR = RB / 16;           // 16-byte slices per row: 8, 16 or 32
+  static constexpr int NKL = SPR / 4;           // MFMA k-chunks per tile = DMA loads per tile
+  static constexpr int TPI = 64 / SPR;          // rows per DMA load instruction
+  static constexpr int KTILE = kTile * RB;      // K bytes of one tile
+  static constexpr int SWZ = (SPR < 16 ? SPR : 16) - 1;
+  static constexpr int VPL = D / 16;            // V elements per lane per token
+  static constexpr int VW = VPL * E / 4;        // V words per lane per token
+  static constexpr int VLD = VW <= 4 ? 1 : VW / 4;   // V load instructions per round
+  static constexpr int LOADS = NKL + 4 * VLD;   // vector-memory instructions per tile
 };
 
-template <int DT, int D, int GP, int NW, bool PARTIAL>
+// LDS of a decode workgroup: per-wave K stages (reused for the wave's epilogue) and p slots.
+template <int DT, int D, int GP, int NW, int DEPTH>
+struct DecodeShared {
+  using Geo = TileGeo<DT, D>;
+  static constexpr int EPI = (GP * D + 3 * GP) * 4;        // o[GP][D], m[GP], l[GP], bad
+  static constexpr int WREG = DEPTH * Geo::KTILE > EPI ? DEPTH * Geo::KTILE : EPI;
+  char w[NW][WREG] __attribute__((aligned(16)));
+  float p[NW][kTile][GP];
+  float a[NW][GP];
+};
+
+// What one wave streams: one KV head of one sequence over logical tokens [t_begin, t_end).
+struct HeadSource {
+  const char* kpool;
+  const char* vpool;
+  const int32_t* table;      // page-table row of the sequence
+  int page_shift, num_pages;
+  int tok_stride;            // bytes between consecutive slots of a page
+  int64_t page_stride;
+  int head_off;              // kvh * row bytes
+  int t_begin, t_end;        // t_begin is a multiple of 16
+  int sub, stride;           // this wave takes tiles sub, sub + stride, ...
+};
+
+template <int DT, int D, int GP, int DEPTH>
+struct HeadPipe {
+  using Geo = TileGeo<DT, D>;
+  static constexpr int NKL = Geo::NKL, VPL = Geo::VPL, VW = Geo::VW;
+
+  // per-lane constants
+  int lane, m16, kq;
+  uint32_t dma_off[NKL];   // byte offset (within a tile of this head) of this lane's DMA slice
+  uint32_t rd_off[NKL];    // LDS offset of this lane's MFMA operand slice
+  uint32_t v_off;          // byte offset of this lane's V dims in round 0
+  uint32_t v_round;        // bytes between rounds (4 tokens)
+  uint32_t lds_base;       // this wave's K stages
+  float* p_slot;           // [16][GP]
+  float* a_slot;           // [GP]
+  // per-head state
+  u32x4 qreg[NKL];
+  float m_run, l_run, o[GP][VPL];
+  bool bad;
+  uint32_t vreg[DEPTH][4][VW];
+
+  __device__ void init(int tok_stride, uint32_t lds, float* p, float* a) {
+    lane = threadIdx.x & 63;
+    m16 = lane & 15;
+    kq = lane >> 4;
+    const int d_row = lane / Geo::SPR, d_pos = lane % Geo::SPR;
+#pragma unroll
+    for (int i = 0; i < NKL; ++i) {
+      const int t_in = Geo::TPI * i + d_row;
+      dma_off[i] = uint32_t(t_in) * tok_stride + uint32_t(d_pos ^ (t_in & Geo::SWZ)) * 16u;
+    }
+#pragma unroll
+    for (int c = 0; c < NKL; ++c)
+      rd_off[c] = uint32_t(m16) * Geo::RB + uint32_t((4 * c + kq) ^ (m16 & Geo::SWZ)) * 16u;
+    v_off = uint32_t(kq) * tok_stride + uint32_t(m16) * VPL * Geo::E;
+    v_round = 4u * tok_stride;
+    lds_base = lds;
+    p_slot = p;
+    a_slot = a;
+  }
+
+  // Q^T operand: lane holds q[head m16][16-byte slices 4c + kq]; zero for padded heads.
+  // `q_group` points at the first query head of the GQA group.
+  __device__ void load_q(const char* q_group, int G) {
+    const char* qrow = q_group + int64_t(m16) * Geo::RB;
+#pragma unroll
+    for (int c = 0; c < NKL; ++c)
+      qreg[c] = (m16 < G) ? *reinterpret_cast<const u32x4*>(qrow + 64 * c + 16 * kq)
+                          : u32x4{0u, 0u, 0u, 0u};
+  }
+
+  __device__ void reset() {
+    m_run = neg_inf();
+    l_run = 0.f;
+#pragma unroll
+    for (int g = 0; g < GP; ++g)
+#pragma unroll
+      for (int e = 0; e < VPL; ++e) o[g][e] = 0.f;
+    bad = false;
+  }
+
+  // Issue one tile: V rows into registers, then K rows into LDS stage `st`.  An out-of-range
+  // page id reads page 0 instead (the tile is then skipped and the head's result is NaN).
+  __device__ void issue(const HeadSource& s, int st, int tile, int page) {
+    const int t0 = s.t_begin + tile * kTile;
+    const int pg = (page >= 0 && page < s.num_pages) ? page : 0;
+    const int64_t base = int64_t(pg) * s.page_stride +
+                         int64_t(t0 & ((1 << s.page_shift) - 1)) * s.tok_stride + s.head_off;
+    const uint32_t kdst = lds_base + uint32_t(st * Geo::KTILE);
+    const gptr vb = uniform_gptr(s.vpool + base);
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) load_words<VW>(vb + v_off + rr * v_round, vreg[st][rr]);
+    const gptr kb = uniform_gptr(s.kpool + base);
+#pragma unroll
+    for (int i = 0; i < NKL; ++i) dma16_to_lds<kDmaPolicy>(kb + dma_off[i], kdst + uint32_t(i * 1024));
+  }
+
+  // Attend to the tile held in stage `st` (its loads have completed).
+  __device__ void process(const HeadSource& s, int st, int tile, float scale_log2, int G) {
+    const int t0 = s.t_begin + tile * kTile;
+    const bool masked = t0 + kTile > s.t_end;
+    const uint32_t ks = lds_base + uint32_t(st * Geo::KTILE);
+
+    // ---- S^T = K . Q^T ---------------------------------------------------------------------
+    u32x4 kops[NKL];
+#pragma unroll
+    for (int c = 0; c < NKL; ++c) kops[c] = lds_read16(ks + rd_off[c]);
+    lds_wait_all<NKL>(kops);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NKL; ++c) {
+      if constexpr (DT == DT_BF16) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kops[c]),
+                                                      __builtin_bit_cast(bf16x8, qreg[c]), acc,
+                                                      0, 0, 0);
+      } else if constexpr (DT == DT_F16) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, kops[c]),
+                                                     __builtin_bit_cast(f16x8, qreg[c]), acc,
+                                                     0, 0, 0);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kops[c][i]),
+                                                     __uint_as_float(qreg[c][i]), acc, 0, 0, 0);
+      }
+    }
+
+    // ---- online softmax (lane: head m16, tokens 4 kq + i) ------------------------------------
+    float sc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sc[i] = acc[i] * scale_log2;
+      if (masked && t0 + 4 * kq + i >= s.t_end) sc[i] = neg_inf();
+    }
+    const float mx = max_rows4(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = fast_exp2(m_run - m_new);
+    float pr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(sc[i] - m_new);
+    l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+    m_run = m_new;
+
+    if (m16 < GP) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p_slot[(4 * kq + i) * GP + m16] = pr[i];
+      if (kq == 0) a_slot[m16] = alpha;
+    }
+    const bool rescale = __ballot(m16 < G && alpha != 1.f) != 0;
+    __builtin_amdgcn_wave_barrier();
+
+    // ---- PV ----------------------------------------------------------------------------------
+    if (rescale) {
+      float a[GP];
+#pragma unroll
+      for (int g = 0; g < GP; ++g) a[g] = a_slot[g];
+#pragma unroll
+      for (int g = 0; g < GP; ++g)
+#pragma unroll
+        for (int e = 0; e < VPL; ++e) o[g][e] *= a[g];
+    }
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      float pg[GP];
+#pragma unroll
+      for (int g = 0; g < GP; ++g) pg[g] = p_slot[(4 * rr + kq) * GP + g];
+      float v[VPL];
+      if constexpr (DT == DT_F32) {
+#pragma unroll
+        for (int e = 0; e < VPL; ++e) v[e] = __uint_as_float(vreg[st][rr][e]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < VPL / 2; ++e) unpack2<DT>(vreg[st][rr][e], v[2 * e], v[2 * e + 1]);
+      }
+      if (masked && t0 + 4 * rr + kq >= s.t_end) {
+#pragma unroll
+        for (int e = 0; e < VPL; ++e) v[e] = 0.f;
+      }
+#pragma unroll
+      for (int g = 0; g < GP; ++g)
+#pragma unroll
+        for (int e = 0; e < VPL; ++e) o[g][e] = fmaf(pg[g], v[e], o[g][e]);
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // All of this wave's tiles: chunks of up to 64 tiles, DEPTH tiles in flight.
+  __device__ void run(const HeadSource& s, float scale_log2, int G) {
+    const int n_tiles = (s.t_end - s.t_begin + kTile - 1) / kTile;
+    const int n_my = n_tiles > s.sub ? (n_tiles - s.sub + s.stride - 1) / s.stride : 0;
+    for (int c0 = 0; c0 < n_my; c0 += kChunk) {
+      const int nc = min(kChunk, n_my - c0);
+      // Lane j holds the page id of this wave's chunk tile min(j, nc - 1).
+      const int jt = c0 + min(lane, nc - 1);
+      const int page_vec = s.table[(s.t_begin + (s.sub + jt * s.stride) * kTile) >> s.page_shift];
+      auto page_at = [&](int k) { return __builtin_amdgcn_readlane(page_vec, min(k, nc - 1)); };
+      auto tile_at = [&](int k) { return s.sub + (c0 + min(k, nc - 1)) * s.stride; };
+      auto ok = [&](int pg) { return pg >= 0 && pg < s.num_pages; };
+
+#pragma unroll
+      for (int d = 0; d < DEPTH; ++d) issue(s, d, tile_at(d), page_at(d));
+      for (int k = 0; k < nc; k += DEPTH) {
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) {
+          // Stage d's loads are the oldest in flight: wait for them on every path.
+          wait_vmcnt<(DEPTH - 1) * Geo::LOADS>();
+          if (k + d < nc) {
+            if (ok(page_at(k + d))) process(s, d, tile_at(k + d), scale_log2, G); else bad = true;
+          }
+          // Refill this stage with the tile DEPTH ahead (clamped to the chunk's last tile, so
+          // the number of loads in flight stays fixed).
+          issue(s, d, tile_at(k + d + DEPTH), page_at(k + d + DEPTH));
+        }
+      }
+      wait_vmcnt<0>();
+    }
+  }
+
+  // Reduce the wave's state across its 4 row groups and store it at `ep` (LDS):
+  // o[GP][D], then m[GP], l[GP], bad.
+  __device__ void to_lds(float* ep) {
+    l_run = sum_rows4(l_run);
+#pragma unroll
+    for (int g = 0; g < GP; ++g)
+#pragma unroll
+      for (int e = 0; e < VPL; ++e) o[g][e] = sum_rows4(o[g][e]);
+    if (lane < 16) {
+#pragma unroll
+      for (int g = 0; g < GP; ++g)
+#pragma unroll
+        for (int e = 0; e < VPL; ++e) ep[g * D + lane * VPL + e] = o[g][e];
+    }
+    if (lane < GP) {
+      ep[GP * D + lane] = m_run;
+      ep[GP * D + GP + lane] = l_run;
+      ep[GP * D + 2 * GP + lane] = bad ? 1.f : 0.f;
+    }
+  }
+};
+
+// Combine the waves that served one head (waves h_in, h_in + hpw, ...) and hand each output
+// element to `emit(h_in, g, d, value, lse, nan)`: value = o / l, lse in natural log.
+template <int D, int GP, int WREG, class Emit>
+__device__ void combine_waves(const char* w_lds, int hpw, int wph, int G, int nthreads, Emit emit) {
+  for (int idx = threadIdx.x; idx < hpw * G * D; idx += nthreads) {
+    const int h_in = idx / (G * D);
+    const int g = (idx / D) % G;
+    const int d = idx % D;
+    float M = neg_inf();
+    float any_bad = 0.f;
+    for (int k = 0; k < wph; ++k) {
+      const float* e = reinterpret_cast<const float*>(w_lds + (h_in + k * hpw) * WREG);
+      M = fmaxf(M, e[GP * D + g]);
+      any_bad += e[GP * D + 2 * GP];
+    }
+    float lsum = 0.f, osum = 0.f;
+    for (int k = 0; k < wph; ++k) {
+      const float* e = reinterpret_cast<const float*>(w_lds + (h_in + k * hpw) * WREG);
+      const float sc = fast_exp2(e[GP * D + g] - M);
+      lsum = fmaf(sc, e[GP * D + GP + g], lsum);
+      osum = fmaf(sc, e[g * D + d], osum);
+    }
+    const bool nan_out = any_bad != 0.f;
+    emit(h_in, g, d, nan_out ? qnan() : osum / lsum,
+         nan_out ? qnan() : (M + __builtin_amdgcn_logf(lsum)) * kLn2, nan_out);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Fixed partitions
+// ---------------------------------------------------------------------------------------------
+
+// One workgroup per (sequence, partition, group of KV heads).  Wave w serves KV head
+// hg * HPW + w % HPW and takes that head's tiles w / HPW, + WPH, ... (HPW heads per workgroup,
+// WPH = NW / HPW waves per head).
+template <int DT, int D, int GP, int NW, int DEPTH, bool PARTIAL>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams p) {
-  constexpr int E = elem_size<DT>();
-  constexpr int NKL = D * E / 64;    // 16-byte K slices per lane per tile
-  constexpr int VPL = D / 16;        // V elements per lane per token
-  constexpr int VW = VPL * E / 4;    // V words per lane per token
+  using Geo = TileGeo<DT, D>;
+  using Shm = DecodeShared<DT, D, GP, NW, DEPTH>;
   static_assert(GP == 4 || GP == 8 || GP == 16, "padded group");
+  static_assert((DEPTH - 1) * Geo::LOADS < 64, "vmcnt range");
+  __shared__ Shm sm;
 
-  __shared__ float p_lds[NW][kTile][GP];
-  __shared__ float a_lds[NW][GP];
-  __shared__ float o_lds[NW][GP][D];
-  __shared__ float m_lds[NW][GP];
-  __shared__ float l_lds[NW][GP];
-  __shared__ int bad_lds[NW];
-
-  const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = p.group;
+  const int HPW = p.heads_per_wg;
+  const int WPH = NW / HPW;
 
-  // ---- work unit ------------------------------------------------------------------------
   int id = blockIdx.x;
-  const int kvh = id % p.hkv;
-  id /= p.hkv;
+  const int nhg = p.hkv / HPW;
+  const int hg = id % nhg;
+  id /= nhg;
   const int b = id % p.batch;
   const int part = PARTIAL ? id / p.batch : 0;
+  const int kvh = hg * HPW + wave % HPW;
 
   const int L = p.context_lens[b];
   int t_begin = 0, t_end = L;
@@ -142,219 +367,254 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams p) {
   } else {
     if (L <= 0 || L > p.capacity) {
       const float fill = L <= 0 ? 0.f : qnan();
-      for (int idx = threadIdx.x; idx < G * D; idx += NW * 64) {
-        const int g = idx / D, d = idx % D;
-        store_elem<DT>(p.out, (int64_t(b) * p.hq + kvh * G + g) * D + d, fill);
+      for (int idx = threadIdx.x; idx < HPW * G * D; idx += NW * 64) {
+        const int h = (hg * HPW + idx / (G * D)) * G + (idx / D) % G;
+        store_elem<DT>(p.out, (int64_t(b) * p.hq + h) * D + idx % D, fill);
       }
       return;
     }
   }
-  const int n_tiles = (t_end - t_begin + kTile - 1) / kTile;
 
-  // ---- per-lane constants -----------------------------------------------------------------
-  const int row = lane & 15;      // MFMA: token row (K) / head column (Q, S)
-  const int kq = lane >> 4;       // MFMA: k-group; PV: token within a round
-  const int head_col = row;
-  const uint32_t head_off = uint32_t(kvh) * D * E;
-  const uint32_t k_off = uint32_t(row) * p.tok_stride + head_off + 16u * kq;
-  const uint32_t v_off = uint32_t(kq) * p.tok_stride + head_off + uint32_t(row) * VPL * E;
-  const uint32_t v_round = 4u * p.tok_stride;
-  const char* const kpool = static_cast<const char*>(p.k_pool);
-  const char* const vpool = static_cast<const char*>(p.v_pool);
-  const int32_t* const table = p.page_table + int64_t(b) * p.max_pages;
-  const int page_mask = (1 << p.page_shift) - 1;
-
-  // Q^T operand: lane holds q[head_col][16-byte slices c * 64 + 16 kq], zero for padded heads.
-  u32x4 qreg[NKL];
-  {
-    const char* qrow = static_cast<const char*>(p.q) +
-                       (int64_t(b) * p.hq + int64_t(kvh) * G + head_col) * D * E;
-#pragma unroll
-    for (int c = 0; c < NKL; ++c) {
-      qreg[c] = (head_col < G) ? *reinterpret_cast<const u32x4*>(qrow + 64 * c + 16 * kq)
-                               : u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-
-  float m_run = neg_inf();   // running max of head `head_col` (base-2 domain)
-  float l_run = 0.f;         // running sum over this lane's rows
-  float o[GP][VPL];
-#pragma unroll
-  for (int g = 0; g < GP; ++g)
-#pragma unroll
-    for (int e = 0; e < VPL; ++e) o[g][e] = 0.f;
-  bool bad = false;
-
-  auto page_of = [&](int tile) -> int {
-    const int t0 = t_begin + tile * kTile;
-    return __builtin_amdgcn_readfirstlane(table[t0 >> p.page_shift]);
-  };
-  auto load_tile = [&](int tile, int page, TileRegs<NKL, VW>& r) {
-    const int t0 = t_begin + tile * kTile;
-    const int64_t base = int64_t(page) * p.page_stride + int64_t(t0 & page_mask) * p.tok_stride;
-    const char* kb = kpool + base;
-    const char* vb = vpool + base;
-#pragma unroll
-    for (int c = 0; c < NKL; ++c) r.k[c] = *reinterpret_cast<const u32x4*>(kb + k_off + 64 * c);
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) load_words<VW>(vb + v_off + rr * v_round, r.v[rr]);
-  };
-  auto page_ok = [&](int page) { return page >= 0 && page < p.num_pages; };
-
-  TileRegs<NKL, VW> cur, nxt;
-  int tile = wave;
-  int page_cur = 0, page_nxt = 0;
-  if (tile < n_tiles) {
-    page_cur = page_of(tile);
-    if (page_ok(page_cur)) load_tile(tile, page_cur, cur);
-  }
-  if (tile + NW < n_tiles) page_nxt = page_of(tile + NW);
-
-  for (; tile < n_tiles; tile += NW) {
-    const int t_next = tile + NW;
-    if (t_next < n_tiles && page_ok(page_nxt)) load_tile(t_next, page_nxt, nxt);
-    const int page_after = (t_next + NW < n_tiles) ? page_of(t_next + NW) : 0;
-
-    if (page_ok(page_cur)) {
-      const int t0 = t_begin + tile * kTile;
-      const bool masked = t0 + kTile > t_end;
-
-      // ---- S^T = K . Q^T -----------------------------------------------------------------
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < NKL; ++c) {
-        if constexpr (DT == DT_BF16) {
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.k[c]),
-                                                        __builtin_bit_cast(bf16x8, qreg[c]), acc,
-                                                        0, 0, 0);
-        } else if constexpr (DT == DT_F16) {
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, cur.k[c]),
-                                                       __builtin_bit_cast(f16x8, qreg[c]), acc,
-                                                       0, 0, 0);
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(cur.k[c][i]),
-                                                       __uint_as_float(qreg[c][i]), acc, 0, 0, 0);
-        }
-      }
-
-      // ---- online softmax (lane: head `head_col`, tokens 4 kq + i) --------------------------
-      float s[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        s[i] = acc[i] * p.scale_log2;
-        if (masked && t0 + 4 * kq + i >= t_end) s[i] = neg_inf();
-      }
-      float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = fast_exp2(m_run - m_new);
-      float pr[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(s[i] - m_new);
-      l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-      m_run = m_new;
-
-      if (head_col < GP) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) p_lds[wave][4 * kq + i][head_col] = pr[i];
-        if (kq == 0) a_lds[wave][head_col] = alpha;
-      }
-      const bool rescale = __ballot(head_col < G && alpha != 1.f) != 0;
-      __builtin_amdgcn_wave_barrier();
-
-      // ---- PV ---------------------------------------------------------------------------
-      if (rescale) {
-        float a[GP];
-#pragma unroll
-        for (int g = 0; g < GP; ++g) a[g] = a_lds[wave][g];
-#pragma unroll
-        for (int g = 0; g < GP; ++g)
-#pragma unroll
-          for (int e = 0; e < VPL; ++e) o[g][e] *= a[g];
-      }
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        float pg[GP];
-#pragma unroll
-        for (int g = 0; g < GP; ++g) pg[g] = p_lds[wave][4 * rr + kq][g];
-        float v[VPL];
-        if constexpr (DT == DT_F32) {
-#pragma unroll
-          for (int e = 0; e < VPL; ++e) v[e] = __uint_as_float(cur.v[rr][e]);
-        } else {
-#pragma unroll
-          for (int e = 0; e < VPL / 2; ++e) unpack2<DT>(cur.v[rr][e], v[2 * e], v[2 * e + 1]);
-        }
-        if (masked && t0 + 4 * rr + kq >= t_end) {
-#pragma unroll
-          for (int e = 0; e < VPL; ++e) v[e] = 0.f;
-        }
-#pragma unroll
-        for (int g = 0; g < GP; ++g)
-#pragma unroll
-          for (int e = 0; e < VPL; ++e) o[g][e] = fmaf(pg[g], v[e], o[g][e]);
-      }
-      __builtin_amdgcn_wave_barrier();
-    } else {
-      bad = true;
-    }
-
-    cur = nxt;
-    page_cur = page_nxt;
-    page_nxt = page_after;
-  }
-
-  // ---- merge the waves ------------------------------------------------------------------
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
-#pragma unroll
-  for (int g = 0; g < GP; ++g)
-#pragma unroll
-    for (int e = 0; e < VPL; ++e) {
-      o[g][e] += __shfl_xor(o[g][e], 16);
-      o[g][e] += __shfl_xor(o[g][e], 32);
-    }
-  if (lane < GP) {
-    m_lds[wave][lane] = m_run;
-    l_lds[wave][lane] = l_run;
-  }
-  if (lane < 16) {
-#pragma unroll
-    for (int g = 0; g < GP; ++g)
-#pragma unroll
-      for (int e = 0; e < VPL; ++e) o_lds[wave][g][lane * VPL + e] = o[g][e];
-  }
-  if (lane == 0) bad_lds[wave] = bad ? 1 : 0;
+  HeadPipe<DT, D, GP, DEPTH> hp;
+  hp.init(p.tok_stride, lds_addr(sm.w[wave]), &sm.p[wave][0][0], &sm.a[wave][0]);
+  hp.load_q(static_cast<const char*>(p.q) + (int64_t(b) * p.hq + int64_t(kvh) * G) * Geo::RB, G);
+  hp.reset();
+  HeadSource src;
+  src.kpool = static_cast<const char*>(p.k_pool);
+  src.vpool = static_cast<const char*>(p.v_pool);
+  src.table = p.page_table + int64_t(b) * p.max_pages;
+  src.page_shift = p.page_shift;
+  src.num_pages = p.num_pages;
+  src.tok_stride = p.tok_stride;
+  src.page_stride = p.page_stride;
+  src.head_off = kvh * Geo::RB;
+  src.t_begin = t_begin;
+  src.t_end = t_end;
+  src.sub = wave / HPW;
+  src.stride = WPH;
+  hp.run(src, p.scale_log2, G);
+  hp.to_lds(reinterpret_cast<float*>(sm.w[wave]));
   __syncthreads();
 
-  int any_bad = 0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) any_bad |= bad_lds[w];
+  combine_waves<D, GP, Shm::WREG>(&sm.w[0][0], HPW, WPH, G, NW * 64,
+      [&](int h_in, int g, int d, float val, float lse, bool) {
+        const int h = (hg * HPW + h_in) * G + g;
+        if constexpr (PARTIAL) {
+          const int64_t rowi = (int64_t(b) * p.hq + h) * p.max_partitions + part;
+          p.partial_out[rowi * D + d] = val;
+          if (d == 0) p.partial_lse[rowi] = lse;
+        } else {
+          store_elem<DT>(p.out, (int64_t(b) * p.hq + h) * D + d, val);
+        }
+      });
+}
 
-  for (int idx = threadIdx.x; idx < G * D; idx += NW * 64) {
-    const int g = idx / D, d = idx % D;
-    float M = neg_inf();
-#pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, m_lds[w][g]);
-    float lsum = 0.f, osum = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float sc = fast_exp2(m_lds[w][g] - M);
-      lsum = fmaf(sc, l_lds[w][g], lsum);
-      osum = fmaf(sc, o_lds[w][g][d], osum);
+// ---------------------------------------------------------------------------------------------
+// Balanced decode step
+// ---------------------------------------------------------------------------------------------
+
+// Tiles attended by sequence b in a step (0 for padding rows and rows whose length exceeds the
+// page table's capacity; the latter get NaN outputs from the merge).
+__device__ inline int step_tiles(const StepParams& p, int b) {
+  const int L = p.a.context_lens[b];
+  const int att = L < 0 ? 0 : L + p.append;
+  if (att <= 0 || att > p.a.capacity) return 0;
+  return (att + kTile - 1) / kTile;
+}
+
+// First tile of workgroup range w: the batch's T tiles are cut into `groups` equal ranges.
+__device__ inline int64_t range_start(int64_t w, int64_t T, int64_t groups) { return w * T / groups; }
+
+// Exclusive prefix sum of step_tiles over the batch into `prefix` (B + 1 entries; the last one
+// is the total).  `scan` is NT ints of scratch.  All threads of the block take part.
+template <int NT>
+__device__ void tile_prefix(const StepParams& p, int* prefix, int* scan) {
+  const int B = p.a.batch;
+  const int tid = threadIdx.x;
+  const int seg = (B + NT - 1) / NT;
+  const int lo = min(B, tid * seg), hi = min(B, lo + seg);
+  int local = 0;
+  for (int b = lo; b < hi; ++b) local += step_tiles(p, b);
+  scan[tid] = local;
+  __syncthreads();
+  for (int off = 1; off < NT; off <<= 1) {
+    const int v = scan[tid] + (tid >= off ? scan[tid - off] : 0);
+    __syncthreads();
+    scan[tid] = v;
+    __syncthreads();
+  }
+  int run = scan[tid] - local;
+  for (int b = lo; b < hi; ++b) {
+    prefix[b] = run;
+    run += step_tiles(p, b);
+  }
+  if (tid == NT - 1) prefix[B] = scan[NT - 1];
+  __syncthreads();
+}
+
+// Number of workgroup ranges that hold tiles of [S, E).
+__device__ inline int pieces_of(int64_t S, int64_t E, int64_t T, int64_t groups) {
+  const int64_t w_lo = ((S + 1) * groups - 1) / T;
+  const int64_t w_hi = (E * groups - 1) / T;
+  int n = 0;
+  for (int64_t w = w_lo; w <= w_hi; ++w)
+    n += max(range_start(w, T, groups), S) < min(range_start(w + 1, T, groups), E);
+  return n;
+}
+
+template <int DT, int D, int GP, int NW, int DEPTH>
+__global__ __launch_bounds__(NW * 64) void step_kernel(const StepParams p) {
+  using Geo = TileGeo<DT, D>;
+  using Shm = DecodeShared<DT, D, GP, NW, DEPTH>;
+  static_assert((DEPTH - 1) * Geo::LOADS < 64, "vmcnt range");
+  __shared__ Shm sm;
+  __shared__ int prefix[kMaxStepBatch + 1];
+  __shared__ int scan[NW * 64];
+
+  const DecodeParams& a = p.a;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int G = a.group;
+  const int HPW = a.heads_per_wg;
+  const int WPH = NW / HPW;
+  const int nhg = a.hkv / HPW;
+  const int hg = blockIdx.x % nhg;
+  const int w = blockIdx.x / nhg;
+  const int kvh = hg * HPW + wave % HPW;
+
+  __shared__ int last_arriver;
+
+  tile_prefix<NW * 64>(p, prefix, scan);
+  const int B = a.batch;
+  const int64_t T = prefix[B];
+  // Rows without tiles (padding, or longer than the page table can address): 0 / NaN outputs,
+  // written by one workgroup each.
+  for (int bb = blockIdx.x; bb < B; bb += gridDim.x) {
+    if (prefix[bb + 1] != prefix[bb]) continue;
+    const bool pad = a.context_lens[bb] < 0 || a.context_lens[bb] + p.append <= 0;
+    for (int i = threadIdx.x; i < a.hq * D; i += NW * 64)
+      store_elem<DT>(p.out, int64_t(bb) * a.hq * D + i, pad ? 0.f : qnan());
+    if (p.lse_out)
+      for (int h = threadIdx.x; h < a.hq; h += NW * 64)
+        p.lse_out[int64_t(bb) * a.hq + h] = pad ? neg_inf() : qnan();
+  }
+  const int lo = int(range_start(w, T, p.groups));
+  const int hi = int(range_start(w + 1, T, p.groups));
+  if (lo >= hi) return;
+
+  // First sequence with tiles at or after `lo`.
+  int b = 0;
+  {
+    int l = 0, r = B;   // find the last b with prefix[b] <= lo
+    while (r - l > 1) {
+      const int m = (l + r) / 2;
+      if (prefix[m] <= lo) l = m; else r = m;
     }
-    const int h = kvh * G + g;
-    const float val = any_bad ? qnan() : osum / lsum;
-    if constexpr (PARTIAL) {
-      const int64_t rowi = (int64_t(b) * p.hq + h) * p.max_partitions + part;
-      p.partial_out[rowi * D + d] = val;
-      if (d == 0) p.partial_lse[rowi] = any_bad ? qnan() : (M + __builtin_amdgcn_logf(lsum)) * kLn2;
-    } else {
-      store_elem<DT>(p.out, (int64_t(b) * p.hq + h) * D + d, val);
+    b = l;
+  }
+
+  HeadPipe<DT, D, GP, DEPTH> hp;
+  hp.init(a.tok_stride, lds_addr(sm.w[wave]), &sm.p[wave][0][0], &sm.a[wave][0]);
+  const int row_bytes = a.hkv * Geo::RB;
+  for (; b < B && prefix[b] < hi; ++b) {
+    const int n_b = prefix[b + 1] - prefix[b];
+    if (n_b == 0) continue;
+    const int tb = max(lo, prefix[b]) - prefix[b];
+    const int te = min(hi, prefix[b + 1]) - prefix[b];
+    const int L = a.context_lens[b];
+    const int att = L + p.append;
+
+    // The workgroup holding the sequence's last tile first writes the appended rows of its
+    // heads into the pool; the barrier (which waits for the stores) orders them before the
+    // tile's loads.  No other workgroup reads that slot in this step.
+    if (p.append && te == n_b) {
+      const int page = a.page_table[int64_t(b) * a.max_pages + (L >> a.page_shift)];
+      if (page >= 0 && page < a.num_pages) {
+        const int64_t dst = int64_t(page) * a.page_stride +
+                            int64_t(L & ((1 << a.page_shift) - 1)) * a.tok_stride +
+                            int64_t(hg) * HPW * Geo::RB;
+        const int64_t srco = int64_t(b) * row_bytes + int64_t(hg) * HPW * Geo::RB;
+        for (int i = threadIdx.x; i < HPW * Geo::RB / 16; i += NW * 64) {
+          const u32x4 kv = *reinterpret_cast<const u32x4*>(static_cast<const char*>(p.k_new) + srco + 16 * i);
+          const u32x4 vv = *reinterpret_cast<const u32x4*>(static_cast<const char*>(p.v_new) + srco + 16 * i);
+          *reinterpret_cast<u32x4*>(static_cast<char*>(p.k_pool_w) + dst + 16 * i) = kv;
+          *reinterpret_cast<u32x4*>(static_cast<char*>(p.v_pool_w) + dst + 16 * i) = vv;
+        }
+      }
+      __syncthreads();
     }
+
+    hp.load_q(static_cast<const char*>(a.q) + (int64_t(b) * a.hq + int64_t(kvh) * G) * Geo::RB, G);
+    hp.reset();
+    HeadSource src;
+    src.kpool = static_cast<const char*>(a.k_pool);
+    src.vpool = static_cast<const char*>(a.v_pool);
+    src.table = a.page_table + int64_t(b) * a.max_pages;
+    src.page_shift = a.page_shift;
+    src.num_pages = a.num_pages;
+    src.tok_stride = a.tok_stride;
+    src.page_stride = a.page_stride;
+    src.head_off = kvh * Geo::RB;
+    src.t_begin = tb * kTile;
+    src.t_end = min(att, te * kTile);
+    src.sub = wave / HPW;
+    src.stride = WPH;
+    hp.run(src, a.scale_log2, G);
+    hp.to_lds(reinterpret_cast<float*>(sm.w[wave]));
+    __syncthreads();
+
+    const bool whole = tb == 0 && te == n_b;   // this workgroup holds all of the sequence
+    const int64_t slot = int64_t(w) + b;
+    combine_waves<D, GP, Shm::WREG>(&sm.w[0][0], HPW, WPH, G, NW * 64,
+        [&](int h_in, int g, int d, float val, float lse, bool) {
+          const int h = (hg * HPW + h_in) * G + g;
+          if (whole) {
+            store_elem<DT>(p.out, (int64_t(b) * a.hq + h) * D + d, val);
+            if (d == 0 && p.lse_out) p.lse_out[int64_t(b) * a.hq + h] = lse;
+          } else {
+            p.ws_out[(slot * a.hq + h) * D + d] = val;
+            if (d == 0) p.ws_lse[slot * a.hq + h] = lse;
+          }
+        });
+
+    if (!whole) {
+      // Count this piece in; the workgroup that brings in the sequence's last piece merges
+      // all of them.  Every thread's release fence makes its partials visible device-wide
+      // (each XCD has its own L2) before the barrier that precedes the count; the merging
+      // workgroup's acquire fences drop stale cached copies before it reads the others'.
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        const int need = pieces_of(prefix[b], prefix[b + 1], T, p.groups);
+        const int old = atomicAdd(&p.ws_count[int64_t(b) * nhg + hg], 1);
+        last_arriver = old == need - 1;
+      }
+      __syncthreads();
+      if (last_arriver) {
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        const int64_t S = prefix[b], E = prefix[b + 1];
+        const int64_t w_lo = ((S + 1) * p.groups - 1) / T;
+        const int64_t w_hi = (E * p.groups - 1) / T;
+        for (int idx = threadIdx.x; idx < HPW * G * D; idx += NW * 64) {
+          const int h = (hg * HPW + idx / (G * D)) * G + (idx / D) % G;
+          const int d = idx % D;
+          float M = neg_inf();
+          for (int64_t v = w_lo; v <= w_hi; ++v)
+            if (max(range_start(v, T, p.groups), S) < min(range_start(v + 1, T, p.groups), E))
+              M = fmaxf(M, p.ws_lse[(v + b) * a.hq + h]);
+          float wsum = 0.f, acc = 0.f;
+          for (int64_t v = w_lo; v <= w_hi; ++v) {
+            if (max(range_start(v, T, p.groups), S) >= min(range_start(v + 1, T, p.groups), E)) continue;
+            const float wt = fast_exp2((p.ws_lse[(v + b) * a.hq + h] - M) * kLog2e);
+            wsum += wt;
+            acc = fmaf(wt, p.ws_out[((v + b) * a.hq + h) * D + d], acc);
+          }
+          store_elem<DT>(p.out, (int64_t(b) * a.hq + h) * D + d, acc / wsum);
+          if (d == 0 && p.lse_out) p.lse_out[int64_t(b) * a.hq + h] = M + __builtin_amdgcn_logf(wsum) * kLn2;
+        }
+        if (threadIdx.x == 0) atomicExch(&p.ws_count[int64_t(b) * nhg + hg], 0);   // ready for the next call
+      }
+    }
+    __syncthreads();   // the LDS epilogue area is reused by the next piece
   }
 }
 
@@ -454,40 +714,67 @@ __global__ __launch_bounds__(1024) void validate_kernel(const ValidateParams p) 
   if (threadIdx.x == 0) *p.device_status = status;
 }
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
+constexpr int kDepth = 2;
 
 template <int DT, int D, int GP>
 hipError_t launch_decode_t(const DecodeParams& p, bool partial, hipStream_t stream) {
-  const int64_t units = int64_t(p.batch) * p.hkv * (partial ? p.max_partitions : 1);
+  const int64_t units = int64_t(p.batch) * (p.hkv / p.heads_per_wg) * (partial ? p.max_partitions : 1);
   if (units == 0) return hipSuccess;
   if (partial)
-    hipLaunchKernelGGL((decode_kernel<DT, D, GP, kWaves, true>), dim3(unsigned(units)),
+    hipLaunchKernelGGL((decode_kernel<DT, D, GP, kWaves, kDepth, true>), dim3(unsigned(units)),
                        dim3(kWaves * 64), 0, stream, p);
   else
-    hipLaunchKernelGGL((decode_kernel<DT, D, GP, kWaves, false>), dim3(unsigned(units)),
+    hipLaunchKernelGGL((decode_kernel<DT, D, GP, kWaves, kDepth, false>), dim3(unsigned(units)),
                        dim3(kWaves * 64), 0, stream, p);
   return hipGetLastError();
 }
 
-template <int DT, int D>
-hipError_t launch_decode_d(const DecodeParams& p, int gp, bool partial, hipStream_t stream) {
-  switch (gp) {
-    case 4: return launch_decode_t<DT, D, 4>(p, partial, stream);
-    case 8: return launch_decode_t<DT, D, 8>(p, partial, stream);
-    case 16: return launch_decode_t<DT, D, 16>(p, partial, stream);
-    default: return hipErrorInvalidValue;
-  }
+template <int DT, int D, int GP>
+hipError_t launch_step_t(const StepParams& p, hipStream_t stream) {
+  const int nhg = p.a.hkv / p.a.heads_per_wg;
+  hipLaunchKernelGGL((step_kernel<DT, D, GP, kWaves, kDepth>), dim3(unsigned(p.groups * nhg)),
+                     dim3(kWaves * 64), 0, stream, p);
+  return hipGetLastError();
 }
 
-template <int DT>
-hipError_t launch_decode_dt(const DecodeParams& p, int head_dim, int gp, bool partial,
-                            hipStream_t stream) {
-  switch (head_dim) {
-    case 64: return launch_decode_d<DT, 64>(p, gp, partial, stream);
-    case 128: return launch_decode_d<DT, 128>(p, gp, partial, stream);
+// Dispatch over (dtype, head_dim, padded group) to a templated launcher F<DT, D, GP>.
+template <template <int, int, int> class F, class P>
+hipError_t dispatch_shape(const P& p, int dtype, int head_dim, int gp, hipStream_t stream, bool flag) {
+#define PKV_GP(DT, D)                                                      \
+  switch (gp) {                                                            \
+    case 4: return F<DT, D, 4>::run(p, stream, flag);                      \
+    case 8: return F<DT, D, 8>::run(p, stream, flag);                      \
+    case 16: return F<DT, D, 16>::run(p, stream, flag);                    \
+    default: return hipErrorInvalidValue;                                  \
+  }
+#define PKV_D(DT)                                                          \
+  switch (head_dim) {                                                      \
+    case 64: PKV_GP(DT, 64)                                                \
+    case 128: PKV_GP(DT, 128)                                              \
+    default: return hipErrorInvalidValue;                                  \
+  }
+  switch (dtype) {
+    case DT_F32: PKV_D(DT_F32)
+    case DT_BF16: PKV_D(DT_BF16)
+    case DT_F16: PKV_D(DT_F16)
     default: return hipErrorInvalidValue;
   }
+#undef PKV_D
+#undef PKV_GP
 }
+
+template <int DT, int D, int GP>
+struct DecodeLaunch {
+  static hipError_t run(const DecodeParams& p, hipStream_t s, bool partial) {
+    return launch_decode_t<DT, D, GP>(p, partial, s);
+  }
+};
+
+template <int DT, int D, int GP>
+struct StepLaunch {
+  static hipError_t run(const StepParams& p, hipStream_t s, bool) { return launch_step_t<DT, D, GP>(p, s); }
+};
 
 template <int DT>
 hipError_t launch_merge_dt(const MergeParams& p, int head_dim, hipStream_t stream) {
@@ -504,14 +791,17 @@ hipError_t launch_merge_dt(const MergeParams& p, int head_dim, hipStream_t strea
 
 }  // namespace
 
+int decode_waves() { return kWaves; }
+
 hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim, int group_pad,
                          bool partial, hipStream_t stream) {
-  switch (dtype) {
-    case DT_F32: return launch_decode_dt<DT_F32>(p, head_dim, group_pad, partial, stream);
-    case DT_BF16: return launch_decode_dt<DT_BF16>(p, head_dim, group_pad, partial, stream);
-    case DT_F16: return launch_decode_dt<DT_F16>(p, head_dim, group_pad, partial, stream);
-    default: return hipErrorInvalidValue;
-  }
+  return dispatch_shape<DecodeLaunch>(p, dtype, head_dim, group_pad, stream, partial);
+}
+
+hipError_t launch_step(const StepParams& p, int dtype, int head_dim, int group_pad,
+                       hipStream_t stream) {
+  if (p.a.batch == 0) return hipSuccess;
+  return dispatch_shape<StepLaunch>(p, dtype, head_dim, group_pad, stream, false);
 }
 
 hipError_t launch_merge(const MergeParams& p, int dtype, int head_dim, hipStream_t stream) {

@@ -20,8 +20,31 @@ struct DecodeParams {
   int32_t batch, hq, hkv, group;
   int32_t num_pages, max_pages, page_shift, capacity;   // capacity = max_pages * page_size
   int32_t partition_tokens, max_partitions;
+  int32_t heads_per_wg;  // KV heads per workgroup (divides hkv and the wave count)
   int32_t tok_stride;    // bytes between consecutive slots of a page (Hkv * D * elem)
   int64_t page_stride;   // bytes per page (page_size * tok_stride)
+};
+
+// Largest batch the balanced step supports (its tile prefix lives in LDS).
+constexpr int kMaxStepBatch = 4096;
+
+// Balanced decode step: `a` carries the attention arguments (heads_per_wg set; the partition
+// fields are unused).  Workspace: piece partials ws_out [(groups + B) * Hq * D], ws_lse
+// [(groups + B) * Hq], per-(sequence, head group) arrival counters ws_count [B * groups of
+// heads] (zero before the first call; every call leaves them at zero).
+struct StepParams {
+  DecodeParams a;
+  const void* k_new;     // null: no append
+  const void* v_new;
+  void* k_pool_w;        // the pools, writable (the appended rows)
+  void* v_pool_w;
+  float* ws_out;
+  float* ws_lse;
+  int32_t* ws_count;
+  void* out;
+  float* lse_out;        // may be null
+  int32_t groups;        // token-range groups per head group
+  int32_t append;        // 1: append k_new/v_new at context_lens[b], attend over +1
 };
 
 struct MergeParams {
@@ -56,6 +79,10 @@ struct ValidateParams {
 // padded GQA group (4, 8 or 16).
 hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim, int group_pad,
                          bool partial, hipStream_t stream);
+// Waves per decode workgroup; heads_per_wg must divide it.
+int decode_waves();
+hipError_t launch_step(const StepParams& p, int dtype, int head_dim, int group_pad,
+                       hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, int dtype, int head_dim, hipStream_t stream);
 hipError_t launch_append(const AppendParams& p, hipStream_t stream);
 hipError_t launch_validate(const ValidateParams& p, hipStream_t stream);

@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 8, names
+    assert len(names) == 10, names
     for n in names:
         assert hasattr(L.lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True, text=True).stdout
@@ -109,6 +109,19 @@ def test_append_and_validate_rejections(L):
     assert v(FAKE, FAKE + 0x1000, -1, 0, FAKE + 0x2000, ctypes.byref(s), None) == -1
     assert v(FAKE, FAKE + 0x1000, 0, 0, 0, ctypes.byref(s), None) == -1
     assert v(0, FAKE + 0x1000, 0, 0, FAKE + 0x2000, ctypes.byref(s), None) == -1
+
+
+def test_step_rejections(L):
+    s = shape(L)
+    step = lambda kn=0, vn=0, ws=FAKE + 0x900000, wsb=1 << 30, out=FAKE + 0x500000, sh=s: L.lib.pkv_paged_decode_step(
+        FAKE, kn, vn, FAKE + 0x100000, FAKE + 0x200000, FAKE + 0x300000, FAKE + 0x400000, 0.1,
+        ws, wsb, out, None, ctypes.byref(sh), None)
+    assert step(kn=FAKE + 0xA00000) == -1            # k_new without v_new
+    assert step(ws=0) == -1
+    assert step(ws=FAKE + 0x900004) == -1             # misaligned workspace
+    assert step(out=FAKE + 0x100000) == -1            # out overlaps k_pool
+    assert step(sh=shape(L, batch=5000)) == -2        # batch above the step's limit
+    assert step(sh=shape(L, batch=0)) == 0
 
 
 def test_workspace_bytes(L):
