@@ -156,10 +156,12 @@ int pkv_paged_kv_append(const void* k_new, const void* v_new, void* k_pool, void
  * through per-sequence arrival counters kept in the workspace.
  *
  * workspace: caller-owned device memory of at least pkv_decode_step_workspace_bytes(shape)
- * bytes (queried on the same device), 16-byte aligned, zero-filled before its first use; every
- * call leaves its counters at zero again, so it can be reused without clearing.  Calls that
- * share a workspace must not run concurrently.  Supports batch <= 4096 (else
- * PKV_EUNSUPPORTED). */
+ * bytes (queried on the same device), 16-byte aligned, zero-filled before its first use.  The
+ * counters sit at its start, sized for the largest batch, and every call leaves them at zero, so
+ * one workspace serves later calls without clearing as long as num_kv_heads stays the same (any
+ * batch up to the one it was sized for); zero it again before using it for another head count.
+ * Calls that share a workspace must not run concurrently.  Supports batch <= 4096 and
+ * num_q_heads <= 1024 (else PKV_EUNSUPPORTED). */
 int pkv_paged_decode_step(const void* q, const void* k_new, const void* v_new, void* k_pool,
                           void* v_pool, const int32_t* page_table, const int32_t* context_lens,
                           float scale, void* workspace, size_t workspace_bytes, void* out,

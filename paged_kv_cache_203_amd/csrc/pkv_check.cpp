@@ -203,10 +203,10 @@ StepWorkspace step_workspace(const pkv_shape& s, int64_t groups, int heads_per_w
   const uint64_t pieces = uint64_t(groups) + uint64_t(s.batch);
   const uint64_t head_groups = uint64_t(s.num_kv_heads / heads_per_wg);
   StepWorkspace w;
-  w.out_off = 0;
-  w.lse_off = up(pieces * s.num_q_heads * s.head_dim * 4);
-  w.count_off = w.lse_off + up(pieces * s.num_q_heads * 4);
-  w.bytes = w.count_off + up(uint64_t(s.batch) * head_groups * 4);
+  w.count_off = 0;
+  w.out_off = up(uint64_t(kMaxStepBatch) * head_groups * 4);
+  w.lse_off = w.out_off + up(pieces * s.num_q_heads * s.head_dim * 4);
+  w.bytes = w.lse_off + up(pieces * s.num_q_heads * 4);
   return w;
 }
 
@@ -216,7 +216,10 @@ int check_step(const void* q, const void* k_new, const void* v_new, const void* 
                const void* out, const float* lse_out, const pkv_shape* s, std::string& msg) {
   int rc = check_shape(s, msg);
   if (rc) return rc;
-  if (s->batch > 4096) return fail(msg, PKV_EUNSUPPORTED, "batch must be <= 4096 for the decode step");
+  if (s->batch > kMaxStepBatch)
+    return fail(msg, PKV_EUNSUPPORTED, "batch must be <= 4096 for the decode step");
+  if (s->num_q_heads > kMaxStepHeads)
+    return fail(msg, PKV_EUNSUPPORTED, "num_q_heads must be <= 1024 for the decode step");
   if (s->batch == 0) return PKV_OK;
   rc = check_attention_inputs(q, k_pool, v_pool, page_table, context_lens, scale, msg);
   if (rc) return rc;

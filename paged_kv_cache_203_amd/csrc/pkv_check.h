@@ -46,11 +46,18 @@ int check_append(const void* k_new, const void* v_new, const void* k_pool, const
                  const int32_t* page_table, const int32_t* context_lens, const pkv_shape* s,
                  std::string& msg);
 
+// Largest batch the balanced decode step supports (its tile prefix lives in LDS), and most query
+// heads (keeps a sequence's piece partials within 32-bit buffer offsets).
+constexpr int kMaxStepBatch = 4096;
+constexpr int kMaxStepHeads = 1024;
+
 // Workspace layout of the balanced decode step for `groups` workgroup ranges (all offsets
-// 256-byte aligned): piece outputs, piece log-sum-exps, arrival counters (one per sequence and
-// group of heads_per_wg KV heads).
+// 256-byte aligned).  The arrival counters (one per sequence and group of heads_per_wg KV heads)
+// come first and are sized for kMaxStepBatch sequences, so their place does not move with the
+// batch: a workspace whose counters are zero stays valid for any batch with the same head
+// layout.  Piece outputs and piece log-sum-exps follow.
 struct StepWorkspace {
-  uint64_t out_off, lse_off, count_off, bytes;
+  uint64_t count_off, out_off, lse_off, bytes;
 };
 StepWorkspace step_workspace(const pkv_shape& s, int64_t groups, int heads_per_wg);
 

@@ -118,12 +118,36 @@ __device__ inline float sum_rows4(float x) {   // sum over lanes {l, l^16, l^32,
   return a + b;
 }
 
-// s_waitcnt that waits until at most `n` vector-memory loads of this wave are outstanding
-// (expcnt and lgkmcnt left at their maxima).
+// s_waitcnt that waits until at most `n` vector-memory operations (loads and stores: gfx9
+// counts both in vmcnt) of this wave are outstanding (expcnt and lgkmcnt left at their maxima).
 template <int N>
 __device__ inline void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Device-scope (agent) relaxed store and load of a float: the access carries the device scope,
+// so it is coherent across the XCDs, whose L2 caches are private, without a cache write-back or
+// invalidate.  Used for values one workgroup hands to another within a launch.
+__device__ inline void dev_store(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline float dev_load(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Buffer resource over `bytes` bytes from `base` (raw addressing, stride 0); loads past the end
+// return zeros.
+typedef __amdgpu_buffer_rsrc_t BufRes;
+__device__ inline BufRes make_bufres(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, int(bytes), 0x00020000);
+}
+
+// 16-byte device-scope load at byte offset `off` of a buffer: the cache-policy operand 16 sets
+// the sc1 bit (device scope), as dev_load does for a single word.
+__device__ inline f32x4 dev_load16(BufRes r, uint32_t off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, int(off), 0, 16);
+  return f32x4{__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w)};
 }
 
 // 16-byte LDS read issued as inline assembly.  The K stages are filled by direct-to-LDS loads

@@ -452,14 +452,95 @@ __device__ void tile_prefix(const StepParams& p, int* prefix, int* scan) {
   __syncthreads();
 }
 
+// Whether workgroup range w holds tiles of [S, E), for w between the ranges of tiles S and E - 1.
+// With at least as many tiles as ranges no range is empty, and every such w qualifies.
+__device__ inline bool holds_piece(int64_t w, int64_t S, int64_t E, int64_t T, int64_t groups) {
+  return T >= groups ||
+         max(range_start(w, T, groups), S) < min(range_start(w + 1, T, groups), E);
+}
+
 // Number of workgroup ranges that hold tiles of [S, E).
 __device__ inline int pieces_of(int64_t S, int64_t E, int64_t T, int64_t groups) {
   const int64_t w_lo = ((S + 1) * groups - 1) / T;
   const int64_t w_hi = (E * groups - 1) / T;
+  if (T >= groups) return int(w_hi - w_lo + 1);
   int n = 0;
-  for (int64_t w = w_lo; w <= w_hi; ++w)
-    n += max(range_start(w, T, groups), S) < min(range_start(w + 1, T, groups), E);
+  for (int64_t w = w_lo; w <= w_hi; ++w) n += holds_piece(w, S, E, T, groups);
   return n;
+}
+
+// Merge of sequence b's pieces for the NH query heads of head group hg:
+// out = sum_p w_p o_p / sum_p w_p with w_p = 2^((lse_p - M) log2 e), pieces in workgroup order.
+// Each thread takes two float4 columns and issues the loads of up to kMU pieces of both at once
+// (16-byte device-scope loads of the partial rows, one device-scope load of each log-sum-exp),
+// carrying a running maximum from one group of pieces to the next.
+template <int DT, int D, int NT>
+__device__ void step_merge(const StepParams& p, int b, int hg, int NH, int64_t S, int64_t E,
+                           int64_t T) {
+  constexpr int kMU = 8, kCols = 2;
+  const DecodeParams& a = p.a;
+  const int64_t w_lo = ((S + 1) * p.groups - 1) / T;
+  const int npc = int((E * p.groups - 1) / T - w_lo + 1);   // candidate ranges
+  const int ncol = NH * (D / 4);
+  // Byte offsets below are relative to the first candidate's partial rows.
+  const int64_t row0 = (w_lo + b) * a.hq;
+  const BufRes rows = make_bufres(p.ws_out + row0 * D, uint32_t(npc) * uint32_t(a.hq * D * 4));
+  for (int c0 = threadIdx.x; c0 < ncol; c0 += NT * kCols) {
+    float m[kCols], l[kCols], o[kCols][4];
+    int h[kCols], d0[kCols];
+#pragma unroll
+    for (int k = 0; k < kCols; ++k) {
+      const int c = min(c0 + k * NT, ncol - 1);   // a spare column repeats the last one
+      h[k] = hg * NH + c / (D / 4);
+      d0[k] = (c % (D / 4)) * 4;
+      m[k] = neg_inf();
+      l[k] = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[k][j] = 0.f;
+    }
+    for (int k0 = 0; k0 < npc; k0 += kMU) {
+      float ls[kCols][kMU];
+      f32x4 vs[kCols][kMU];
+#pragma unroll
+      for (int u = 0; u < kMU; ++u) {
+        const bool ok = k0 + u < npc && holds_piece(w_lo + k0 + u, S, E, T, p.groups);
+#pragma unroll
+        for (int k = 0; k < kCols; ++k) {
+          const int64_t row = int64_t(k0 + u) * a.hq + h[k];
+          ls[k][u] = ok ? dev_load(&p.ws_lse[row0 + row]) : neg_inf();
+          vs[k][u] = ok ? dev_load16(rows, uint32_t(row * D + d0[k]) * 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < kCols; ++k) {
+        float mc = m[k];
+#pragma unroll
+        for (int u = 0; u < kMU; ++u) mc = fmaxf(mc, ls[k][u]);
+        const float r = fast_exp2((m[k] - mc) * kLog2e);
+        l[k] *= r;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[k][j] *= r;
+#pragma unroll
+        for (int u = 0; u < kMU; ++u) {
+          const float wt = fast_exp2((ls[k][u] - mc) * kLog2e);
+          l[k] += wt;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) o[k][j] = fmaf(wt, vs[k][u][j], o[k][j]);
+        }
+        m[k] = mc;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kCols; ++k) {
+      const int c = c0 + k * NT;
+      if (c >= ncol) continue;
+      const int64_t base = (int64_t(b) * a.hq + h[k]) * D + d0[k];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) store_elem<DT>(p.out, base + j, o[k][j] / l[k]);
+      if (d0[k] == 0 && p.lse_out)
+        p.lse_out[int64_t(b) * a.hq + h[k]] = m[k] + __builtin_amdgcn_logf(l[k]) * kLn2;
+    }
+  }
 }
 
 template <int DT, int D, int GP, int NW, int DEPTH>
@@ -481,7 +562,8 @@ __global__ __launch_bounds__(NW * 64) void step_kernel(const StepParams p) {
   const int w = blockIdx.x / nhg;
   const int kvh = hg * HPW + wave % HPW;
 
-  __shared__ int last_arriver;
+  __shared__ int merging[2];
+  int split_first = -1, split_last = -1;   // sequences whose piece here is split
 
   tile_prefix<NW * 64>(p, prefix, scan);
   const int B = a.batch;
@@ -570,51 +652,48 @@ __global__ __launch_bounds__(NW * 64) void step_kernel(const StepParams p) {
           if (whole) {
             store_elem<DT>(p.out, (int64_t(b) * a.hq + h) * D + d, val);
             if (d == 0 && p.lse_out) p.lse_out[int64_t(b) * a.hq + h] = lse;
-          } else {
-            p.ws_out[(slot * a.hq + h) * D + d] = val;
-            if (d == 0) p.ws_lse[slot * a.hq + h] = lse;
+          } else {   // device-scope stores: written through to where every XCD reads
+            dev_store(&p.ws_out[(slot * a.hq + h) * D + d], val);
+            if (d == 0) dev_store(&p.ws_lse[slot * a.hq + h], lse);
           }
         });
 
-    if (!whole) {
-      // Count this piece in; the workgroup that brings in the sequence's last piece merges
-      // all of them.  Every thread's release fence makes its partials visible device-wide
-      // (each XCD has its own L2) before the barrier that precedes the count; the merging
-      // workgroup's acquire fences drop stale cached copies before it reads the others'.
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-      __syncthreads();
-      if (threadIdx.x == 0) {
-        const int need = pieces_of(prefix[b], prefix[b + 1], T, p.groups);
-        const int old = atomicAdd(&p.ws_count[int64_t(b) * nhg + hg], 1);
-        last_arriver = old == need - 1;
-      }
-      __syncthreads();
-      if (last_arriver) {
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        const int64_t S = prefix[b], E = prefix[b + 1];
-        const int64_t w_lo = ((S + 1) * p.groups - 1) / T;
-        const int64_t w_hi = (E * p.groups - 1) / T;
-        for (int idx = threadIdx.x; idx < HPW * G * D; idx += NW * 64) {
-          const int h = (hg * HPW + idx / (G * D)) * G + (idx / D) % G;
-          const int d = idx % D;
-          float M = neg_inf();
-          for (int64_t v = w_lo; v <= w_hi; ++v)
-            if (max(range_start(v, T, p.groups), S) < min(range_start(v + 1, T, p.groups), E))
-              M = fmaxf(M, p.ws_lse[(v + b) * a.hq + h]);
-          float wsum = 0.f, acc = 0.f;
-          for (int64_t v = w_lo; v <= w_hi; ++v) {
-            if (max(range_start(v, T, p.groups), S) >= min(range_start(v + 1, T, p.groups), E)) continue;
-            const float wt = fast_exp2((p.ws_lse[(v + b) * a.hq + h] - M) * kLog2e);
-            wsum += wt;
-            acc = fmaf(wt, p.ws_out[((v + b) * a.hq + h) * D + d], acc);
-          }
-          store_elem<DT>(p.out, (int64_t(b) * a.hq + h) * D + d, acc / wsum);
-          if (d == 0 && p.lse_out) p.lse_out[int64_t(b) * a.hq + h] = M + __builtin_amdgcn_logf(wsum) * kLn2;
-        }
-        if (threadIdx.x == 0) atomicExch(&p.ws_count[int64_t(b) * nhg + hg], 0);   // ready for the next call
-      }
+    if (!whole) {   // a split piece starts or ends the range
+      if (tb > 0) split_first = b;
+      else split_last = b;
     }
     __syncthreads();   // the LDS epilogue area is reused by the next piece
+  }
+
+  // Count the split pieces in (at most two: the range's first and last); the workgroup that
+  // brings in a sequence's last piece merges all of its pieces.  This is deferred to the end of
+  // the range so that no workgroup stalls between pieces.  The partials were written, and are
+  // read, with device-scope accesses, which are coherent across the XCDs (each has its own L2)
+  // without an L2 write-back or invalidate: each thread waits until its stores are complete,
+  // the barrier orders that before the increments, and a merging workgroup issues its loads
+  // only after it has read the final count.
+  if (split_first < 0 && split_last < 0) return;
+  wait_vmcnt<0>();
+  __syncthreads();
+  if (threadIdx.x < 2) {
+    const int sb = threadIdx.x == 0 ? split_first : split_last;
+    int last = 0;
+    if (sb >= 0) {
+      const int need = pieces_of(prefix[sb], prefix[sb + 1], T, p.groups);
+      const int old = __hip_atomic_fetch_add(&p.ws_count[int64_t(sb) * nhg + hg], 1,
+                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      last = old == need - 1;
+    }
+    merging[threadIdx.x] = last;
+  }
+  __syncthreads();
+  for (int i = 0; i < 2; ++i) {
+    const int sb = i == 0 ? split_first : split_last;
+    if (!merging[i]) continue;
+    step_merge<DT, D, NW * 64>(p, sb, hg, HPW * a.group, prefix[sb], prefix[sb + 1], T);
+    if (threadIdx.x == 0)   // ready for the next call
+      __hip_atomic_store(&p.ws_count[int64_t(sb) * nhg + hg], 0, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 

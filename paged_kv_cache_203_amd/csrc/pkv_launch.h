@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "pkv_check.h"
+
 namespace pkv {
 
 struct DecodeParams {
@@ -25,13 +27,10 @@ struct DecodeParams {
   int64_t page_stride;   // bytes per page (page_size * tok_stride)
 };
 
-// Largest batch the balanced step supports (its tile prefix lives in LDS).
-constexpr int kMaxStepBatch = 4096;
-
 // Balanced decode step: `a` carries the attention arguments (heads_per_wg set; the partition
-// fields are unused).  Workspace: piece partials ws_out [(groups + B) * Hq * D], ws_lse
-// [(groups + B) * Hq], per-(sequence, head group) arrival counters ws_count [B * groups of
-// heads] (zero before the first call; every call leaves them at zero).
+// fields are unused).  Workspace (laid out by step_workspace): per-(sequence, head group)
+// arrival counters ws_count (zero before the first call; every call leaves them at zero),
+// piece partials ws_out [(groups + B) * Hq * D] and ws_lse [(groups + B) * Hq].
 struct StepParams {
   DecodeParams a;
   const void* k_new;     // null: no append

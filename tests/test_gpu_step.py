@@ -158,3 +158,46 @@ def test_step_matches_split_path_within_rounding(pkv):
                                          256, d.scale)
     torch.cuda.synchronize()
     assert np.abs(to_f64(a) - to_f64(b)).max() <= 2 ** -8
+
+
+def test_step_workspace_reused_across_calls(pkv):
+    """The arrival counters return to zero: one zero-filled workspace serves call after call,
+    including a smaller batch after a larger one."""
+    big = W.make_workload(W.config(2).scaled(batch=24, lengths=("uniform", 200, 3000)))
+    small = W.make_workload(W.config(2).scaled(batch=5, lengths=("uniform", 40, 900)), seed=7)
+    db, ds = DeviceWorkload(big), DeviceWorkload(small)
+    ws = torch.zeros(pkv.decode_step_workspace_bytes(db.q, db.k_pool, db.page_table),
+                     dtype=torch.uint8, device="cuda")
+    ref_b, _ = oracle_for(big, (big.k_pool, big.v_pool))
+    ref_s, _ = oracle_for(small, (small.k_pool, small.v_pool))
+    for rep in range(3):
+        for d, w, ref in ((db, big, ref_b), (ds, small, ref_s)):
+            out = pkv.paged_decode_step(d.q, d.k_pool, d.v_pool, d.page_table, d.context_lens,
+                                        d.scale, workspace=ws)
+            torch.cuda.synchronize()
+            assert_parity(to_f64(out), ref, w.dtype, f"step reuse {rep} batch={w.q.shape[0]}")
+
+
+def test_step_repeated_calls_bitwise_stable(pkv):
+    """Pieces hand their partials to the merging workgroup through device-scope accesses.  Calls
+    alternate between two queries on one workspace, so a merge that read a stale cached partial
+    (from the previous call) would change bits; every call must repeat its first result."""
+    w = W.make_workload(W.config(2).scaled(batch=32, lengths=("uniform", 300, 4096)))
+    d = DeviceWorkload(w)
+    q2 = torch.flip(d.q, dims=[0]).contiguous()
+    ws = torch.zeros(pkv.decode_step_workspace_bytes(d.q, d.k_pool, d.page_table),
+                     dtype=torch.uint8, device="cuda")
+    outs = [torch.empty_like(d.q) for _ in range(2)]
+    first = []
+    for rep in range(40):
+        for j, q in enumerate((d.q, q2)):
+            pkv.paged_decode_step(q, d.k_pool, d.v_pool, d.page_table, d.context_lens, d.scale,
+                                  out=outs[j], workspace=ws)
+        torch.cuda.synchronize()
+        if rep == 0:
+            first = [o.clone() for o in outs]
+            ref, _ = oracle_for(w, (w.k_pool, w.v_pool))
+            assert_parity(to_f64(first[0]), ref, w.dtype, "step repeated (first call)")
+        else:
+            for j in range(2):
+                assert torch.equal(outs[j].view(torch.int16), first[j].view(torch.int16)), (rep, j)
