@@ -160,12 +160,23 @@ __device__ inline u32x4 lds_read16(uint32_t lds_addr) {
   return r;
 }
 
+// 4-byte LDS write issued as inline assembly, for values that lanes of one wave hand to each
+// other while direct-to-LDS loads are in flight: as with lds_read16, the compiler does not see it
+// as an LDS access and so does not make it wait for those loads.  lds_wait_writes() orders it
+// before later reads of the same wave.
+__device__ inline void lds_write32(uint32_t lds_addr, float v) {
+  asm volatile("ds_write_b32 %0, %1" : : "v"(lds_addr), "v"(v));
+}
+__device__ inline void lds_wait_writes() { asm volatile("s_waitcnt lgkmcnt(0)"); }
+
 // s_waitcnt lgkmcnt(0) that the compiler cannot schedule uses of `r` above: the registers are
 // operands of the waiting instruction.
 template <int N>
 __device__ inline void lds_wait_all(u32x4 (&r)[N]) {
-  static_assert(N == 2 || N == 4 || N == 8, "operand count");
-  if constexpr (N == 2) {
+  static_assert(N == 1 || N == 2 || N == 4 || N == 8, "operand count");
+  if constexpr (N == 1) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r[0]));
+  } else if constexpr (N == 2) {
     asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r[0]), "+v"(r[1]));
   } else if constexpr (N == 4) {
     asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]));

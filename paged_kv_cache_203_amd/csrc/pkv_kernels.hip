@@ -65,8 +65,8 @@ struct DecodeShared {
   static constexpr int EPI = (GP * D + 3 * GP) * 4;        // o[GP][D], m[GP], l[GP], bad
   static constexpr int WREG = DEPTH * Geo::KTILE > EPI ? DEPTH * Geo::KTILE : EPI;
   char w[NW][WREG] __attribute__((aligned(16)));
-  float p[NW][kTile][GP];
-  float a[NW][GP];
+  float p[NW][kTile][GP] __attribute__((aligned(16)));   // rows read 16 bytes at a time
+  float a[NW][GP] __attribute__((aligned(16)));
 };
 
 // What one wave streams: one KV head of one sequence over logical tokens [t_begin, t_end).
@@ -94,8 +94,8 @@ struct HeadPipe {
   uint32_t v_off;          // byte offset of this lane's V dims in round 0
   uint32_t v_round;        // bytes between rounds (4 tokens)
   uint32_t lds_base;       // this wave's K stages
-  float* p_slot;           // [16][GP]
-  float* a_slot;           // [GP]
+  uint32_t p_lds;          // LDS address of this wave's p[16][GP]: a tile's probabilities
+  uint32_t a_lds;          // LDS address of this wave's a[GP]: the tile's rescale factors
   // per-head state
   u32x4 qreg[NKL];
   float m_run, l_run, o[GP][VPL];
@@ -118,8 +118,8 @@ struct HeadPipe {
     v_off = uint32_t(kq) * tok_stride + uint32_t(m16) * VPL * Geo::E;
     v_round = 4u * tok_stride;
     lds_base = lds;
-    p_slot = p;
-    a_slot = a;
+    p_lds = lds_addr(p);
+    a_lds = lds_addr(a);
   }
 
   // Q^T operand: lane holds q[head m16][16-byte slices 4c + kq]; zero for padded heads.
@@ -204,29 +204,47 @@ struct HeadPipe {
     l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
     m_run = m_new;
 
+    // The probabilities move from the score layout (lane: head m16, tokens 4 kq + i) to the PV
+    // layout (lane: dims of token row 4 rr + kq, all heads) through the wave's LDS slots.  These
+    // accesses are inline assembly (lds_write32 / lds_read16), so the compiler does not make them
+    // wait for the direct-to-LDS K loads in flight, which never touch these slots.
     if (m16 < GP) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) p_slot[(4 * kq + i) * GP + m16] = pr[i];
-      if (kq == 0) a_slot[m16] = alpha;
+      for (int i = 0; i < 4; ++i) lds_write32(p_lds + uint32_t((4 * kq + i) * GP + m16) * 4u, pr[i]);
+      if (kq == 0) lds_write32(a_lds + uint32_t(m16) * 4u, alpha);
     }
     const bool rescale = __ballot(m16 < G && alpha != 1.f) != 0;
+    lds_wait_writes();
     __builtin_amdgcn_wave_barrier();
 
     // ---- PV ----------------------------------------------------------------------------------
+    constexpr int NR = GP / 4;               // 16-byte reads per row of p (or of a)
     if (rescale) {
-      float a[GP];
+      u32x4 av[NR];
 #pragma unroll
-      for (int g = 0; g < GP; ++g) a[g] = a_slot[g];
+      for (int c = 0; c < NR; ++c) av[c] = lds_read16(a_lds + 16u * c);
+      lds_wait_all<NR>(av);
 #pragma unroll
       for (int g = 0; g < GP; ++g)
 #pragma unroll
-        for (int e = 0; e < VPL; ++e) o[g][e] *= a[g];
+        for (int e = 0; e < VPL; ++e) o[g][e] *= __uint_as_float(av[g / 4][g % 4]);
     }
+    constexpr int RPW = NR <= 2 ? 4 : 2;     // rows of p read per wait
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
+    for (int r0 = 0; r0 < 4; r0 += RPW) {
+      u32x4 pv[RPW * NR];
+#pragma unroll
+      for (int j = 0; j < RPW; ++j)
+#pragma unroll
+        for (int c = 0; c < NR; ++c)
+          pv[j * NR + c] = lds_read16(p_lds + uint32_t((4 * (r0 + j) + kq) * GP + 4 * c) * 4u);
+      lds_wait_all<RPW * NR>(pv);
+#pragma unroll
+      for (int j = 0; j < RPW; ++j) {
+      const int rr = r0 + j;
       float pg[GP];
 #pragma unroll
-      for (int g = 0; g < GP; ++g) pg[g] = p_slot[(4 * rr + kq) * GP + g];
+      for (int g = 0; g < GP; ++g) pg[g] = __uint_as_float(pv[j * NR + g / 4][g % 4]);
       float v[VPL];
       if constexpr (DT == DT_F32) {
 #pragma unroll
@@ -243,11 +261,24 @@ struct HeadPipe {
       for (int g = 0; g < GP; ++g)
 #pragma unroll
         for (int e = 0; e < VPL; ++e) o[g][e] = fmaf(pg[g], v[e], o[g][e]);
+      }
     }
     __builtin_amdgcn_wave_barrier();
   }
 
   // All of this wave's tiles: chunks of up to 64 tiles, DEPTH tiles in flight.
+  // Wait until the oldest stage in flight has landed, given that `later` stages were issued
+  // after it (at most N): every load but the newest later * LOADS has completed.
+  template <int N>
+  __device__ static void wait_stage(int later) {
+    if constexpr (N == 0) {
+      wait_vmcnt<0>();
+    } else {
+      if (later >= N) wait_vmcnt<N * Geo::LOADS>();
+      else wait_stage<N - 1>(later);
+    }
+  }
+
   __device__ void run(const HeadSource& s, float scale_log2, int G) {
     const int n_tiles = (s.t_end - s.t_begin + kTile - 1) / kTile;
     const int n_my = n_tiles > s.sub ? (n_tiles - s.sub + s.stride - 1) / s.stride : 0;
@@ -260,22 +291,34 @@ struct HeadPipe {
       auto tile_at = [&](int k) { return s.sub + (c0 + min(k, nc - 1)) * s.stride; };
       auto ok = [&](int pg) { return pg >= 0 && pg < s.num_pages; };
 
+      // The first DEPTH stages are always loaded (a chunk shorter than DEPTH tiles repeats its
+      // last tile), so that the count of loads in flight is the same on every path into the loop.
 #pragma unroll
       for (int d = 0; d < DEPTH; ++d) issue(s, d, tile_at(d), page_at(d));
-      for (int k = 0; k < nc; k += DEPTH) {
+      int k = 0;
+      // Steady state: every stage is refilled with a tile of the chunk, so the loads issued
+      // after stage d's are always those of DEPTH - 1 stages.
+      for (; k + 2 * DEPTH <= nc; k += DEPTH) {
 #pragma unroll
         for (int d = 0; d < DEPTH; ++d) {
-          // Stage d's loads are the oldest in flight: wait for them on every path.
           wait_vmcnt<(DEPTH - 1) * Geo::LOADS>();
-          if (k + d < nc) {
-            if (ok(page_at(k + d))) process(s, d, tile_at(k + d), scale_log2, G); else bad = true;
-          }
-          // Refill this stage with the tile DEPTH ahead (clamped to the chunk's last tile, so
-          // the number of loads in flight stays fixed).
+          if (ok(page_at(k + d))) process(s, d, tile_at(k + d), scale_log2, G); else bad = true;
           issue(s, d, tile_at(k + d + DEPTH), page_at(k + d + DEPTH));
         }
       }
-      wait_vmcnt<0>();
+      // Tail: only tiles of the chunk are loaded, so the loads issued after stage d's (tile
+      // k + d) are those of tiles k + d + 1 ... k + d + DEPTH - 1 that exist.
+      for (; k < nc; k += DEPTH) {
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) {
+          wait_stage<DEPTH - 1>(nc - 1 - (k + d));
+          if (k + d < nc) {
+            if (ok(page_at(k + d))) process(s, d, tile_at(k + d), scale_log2, G); else bad = true;
+          }
+          if (k + d + DEPTH < nc) issue(s, d, tile_at(k + d + DEPTH), page_at(k + d + DEPTH));
+        }
+      }
+      wait_vmcnt<0>();   // nothing is in flight here; this states it for the next chunk
     }
   }
 
