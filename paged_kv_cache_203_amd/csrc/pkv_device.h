@@ -58,6 +58,53 @@ __device__ inline void store_elem(void* base, int64_t idx, float x) {
   }
 }
 
+// Element x rounded to the storage type, as raw bits (bf16: round to nearest even, NaN kept).
+template <int DT>
+__device__ inline uint32_t elem_bits(float x) {
+  if constexpr (DT == DT_F32) {
+    return __float_as_uint(x);
+  } else if constexpr (DT == DT_BF16) {
+    const uint32_t u = __float_as_uint(x);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  } else {
+    const _Float16 h = static_cast<_Float16>(x);
+    return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h));
+  }
+}
+
+// N consecutive elements (8 bytes, or a multiple of 16) stored at base[idx...], rounded as
+// store_elem rounds them, with 8- or 16-byte stores; base + idx must be aligned to that size.
+template <int DT, int N>
+__device__ inline void store_row(void* base, int64_t idx, const float (&x)[N]) {
+  constexpr int E = elem_size<DT>();
+  static_assert(N * E == 8 || (N * E) % 16 == 0, "whole 8- or 16-byte stores");
+  char* dst = static_cast<char*>(base) + idx * E;
+  if constexpr (N * E == 8) {
+    u32x2 w;
+    if constexpr (E == 4) {
+      w = u32x2{elem_bits<DT>(x[0]), elem_bits<DT>(x[1])};
+    } else {
+      w = u32x2{elem_bits<DT>(x[0]) | (elem_bits<DT>(x[1]) << 16), elem_bits<DT>(x[2]) | (elem_bits<DT>(x[3]) << 16)};
+    }
+    *reinterpret_cast<u32x2*>(dst) = w;
+    return;
+  }
+#pragma unroll
+  for (int c = 0; c < (N * E) / 16; ++c) {
+    u32x4 w;
+    if constexpr (E == 4) {
+      w = u32x4{elem_bits<DT>(x[4 * c]), elem_bits<DT>(x[4 * c + 1]), elem_bits<DT>(x[4 * c + 2]),
+                elem_bits<DT>(x[4 * c + 3])};
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        w[i] = elem_bits<DT>(x[8 * c + 2 * i]) | (elem_bits<DT>(x[8 * c + 2 * i + 1]) << 16);
+    }
+    *reinterpret_cast<u32x4*>(dst + 16 * c) = w;
+  }
+}
+
 // Global-address-space byte pointer (loads through it are global_load, never flat_load).
 typedef const __attribute__((address_space(1))) char* gptr;
 typedef const __attribute__((address_space(1))) u32x4* gptr_u32x4;
@@ -143,11 +190,19 @@ __device__ inline BufRes make_bufres(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, int(bytes), 0x00020000);
 }
 
+// 16-byte device-scope store of floats at byte offset `off` of a buffer (16-byte aligned);
+// cache-policy 16 sets the sc1 bit, as dev_store does for a single word.
+__device__ inline void dev_store16(BufRes r, uint32_t off, f32x4 v);
+
 // 16-byte device-scope load at byte offset `off` of a buffer: the cache-policy operand 16 sets
 // the sc1 bit (device scope), as dev_load does for a single word.
 __device__ inline f32x4 dev_load16(BufRes r, uint32_t off) {
   const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, int(off), 0, 16);
   return f32x4{__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w)};
+}
+__device__ inline void dev_store16(BufRes r, uint32_t off, f32x4 v) {
+  const u32x4 w = {__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)};
+  __builtin_amdgcn_raw_buffer_store_b128(w, r, int(off), 0, 16);
 }
 
 // 16-byte LDS read issued as inline assembly.  The K stages are filled by direct-to-LDS loads
@@ -168,6 +223,48 @@ __device__ inline void lds_write32(uint32_t lds_addr, float v) {
   asm volatile("ds_write_b32 %0, %1" : : "v"(lds_addr), "v"(v));
 }
 __device__ inline void lds_wait_writes() { asm volatile("s_waitcnt lgkmcnt(0)"); }
+
+// 8-byte LDS read issued as inline assembly (same rules as lds_read16).
+__device__ inline u32x2 lds_read8(uint32_t lds_addr) {
+  u32x2 r;
+  asm volatile("ds_read_b64 %0, %1" : "=v"(r) : "v"(lds_addr));
+  return r;
+}
+
+// s_waitcnt lgkmcnt(0) for reads issued with lds_read8/16; each value read is then passed
+// through lds_pin(), which the compiler cannot move above the wait (both are volatile asm), so
+// no use of the value can be scheduled before the data has landed.
+__device__ inline void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)"); }
+template <class T>
+__device__ inline void lds_pin(T& r) { asm volatile("" : "+v"(r)); }
+
+// This lane's V bytes of one token row (8, 16 or 32) read from LDS as 32-bit words.
+template <int VB>
+struct LdsRows;
+template <>
+struct LdsRows<8> {
+  u32x2 r;
+  __device__ void read(uint32_t a) { r = lds_read8(a); }
+  __device__ void pin() { lds_pin(r); }
+  __device__ void words(uint32_t (&w)[2]) const { w[0] = r.x; w[1] = r.y; }
+};
+template <>
+struct LdsRows<16> {
+  u32x4 r;
+  __device__ void read(uint32_t a) { r = lds_read16(a); }
+  __device__ void pin() { lds_pin(r); }
+  __device__ void words(uint32_t (&w)[4]) const { w[0] = r.x; w[1] = r.y; w[2] = r.z; w[3] = r.w; }
+};
+template <>
+struct LdsRows<32> {
+  u32x4 r0, r1;
+  __device__ void read(uint32_t a) { r0 = lds_read16(a); r1 = lds_read16(a + 16); }
+  __device__ void pin() { lds_pin(r0); lds_pin(r1); }
+  __device__ void words(uint32_t (&w)[8]) const {
+    w[0] = r0.x; w[1] = r0.y; w[2] = r0.z; w[3] = r0.w;
+    w[4] = r1.x; w[5] = r1.y; w[6] = r1.z; w[7] = r1.w;
+  }
+};
 
 // s_waitcnt lgkmcnt(0) that the compiler cannot schedule uses of `r` above: the registers are
 // operands of the waiting instruction.

@@ -53,17 +53,24 @@ struct TileGeo {
   static constexpr int KTILE = kTile * RB;      // K bytes of one tile
   static constexpr int SWZ = (SPR < 16 ? SPR : 16) - 1;
   static constexpr int VPL = D / 16;            // V elements per lane per token
-  static constexpr int VW = VPL * E / 4;        // V words per lane per token
-  static constexpr int VLD = VW <= 4 ? 1 : VW / 4;   // V load instructions per round
-  static constexpr int LOADS = NKL + 4 * VLD;   // vector-memory instructions per tile
+  static constexpr int VB = VPL * E;            // V bytes per lane per token: 8, 16 or 32
+  static constexpr int VW = VB / 4;             // ... in 32-bit words
+  static constexpr int LOADS = 2 * NKL;         // vector-memory instructions per tile (K, V)
 };
 
-// LDS of a decode workgroup: per-wave K stages (reused for the wave's epilogue) and p slots.
+// Tiles in flight per wave: two, except where two K and V stages of eight waves would not fit
+// in LDS (fp32, head_dim 128).
+template <int DT, int D>
+constexpr int pipe_depth() { return DT == DT_F32 && D == 128 ? 1 : 2; }
+
+// LDS of a decode workgroup: per-wave K and V stages (reused for the wave's epilogue) and p
+// slots.
 template <int DT, int D, int GP, int NW, int DEPTH>
 struct DecodeShared {
   using Geo = TileGeo<DT, D>;
   static constexpr int EPI = (GP * D + 3 * GP) * 4;        // o[GP][D], m[GP], l[GP], bad
-  static constexpr int WREG = DEPTH * Geo::KTILE > EPI ? DEPTH * Geo::KTILE : EPI;
+  static constexpr int STAGES = 2 * DEPTH * Geo::KTILE;    // K stages, then V stages
+  static constexpr int WREG = STAGES > EPI ? STAGES : EPI;
   char w[NW][WREG] __attribute__((aligned(16)));
   float p[NW][kTile][GP] __attribute__((aligned(16)));   // rows read 16 bytes at a time
   float a[NW][GP] __attribute__((aligned(16)));
@@ -80,27 +87,32 @@ struct HeadSource {
   int head_off;              // kvh * row bytes
   int t_begin, t_end;        // t_begin is a multiple of 16
   int sub, stride;           // this wave takes tiles sub, sub + stride, ...
+  const char* q_group;       // q rows of the wave's GQA group (used by HeadPipe::prefetch)
 };
 
 template <int DT, int D, int GP, int DEPTH>
 struct HeadPipe {
   using Geo = TileGeo<DT, D>;
   static constexpr int NKL = Geo::NKL, VPL = Geo::VPL, VW = Geo::VW;
+  static constexpr uint32_t VSTAGE0 = DEPTH * Geo::KTILE;   // LDS offset of V stage 0
 
   // per-lane constants
   int lane, m16, kq;
-  uint32_t dma_off[NKL];   // byte offset (within a tile of this head) of this lane's DMA slice
+  uint32_t dma_off[NKL];   // byte offset (within a tile of this head) of this lane's K slice
+  uint32_t vdma_off[NKL];  // ... and of its V slice (V stages are not swizzled)
   uint32_t rd_off[NKL];    // LDS offset of this lane's MFMA operand slice
-  uint32_t v_off;          // byte offset of this lane's V dims in round 0
-  uint32_t v_round;        // bytes between rounds (4 tokens)
-  uint32_t lds_base;       // this wave's K stages
+  uint32_t v_rd;           // LDS offset (within a V stage) of this lane's dims of row kq
+  uint32_t lds_base;       // this wave's K stages, then its V stages
   uint32_t p_lds;          // LDS address of this wave's p[16][GP]: a tile's probabilities
   uint32_t a_lds;          // LDS address of this wave's a[GP]: the tile's rescale factors
   // per-head state
   u32x4 qreg[NKL];
+  // What prefetch() loaded for the next run(): its q operand and its first chunk's page ids.
+  u32x4 q_pref[NKL];
+  int pv_pref;
+  bool pref_ready = false;
   float m_run, l_run, o[GP][VPL];
   bool bad;
-  uint32_t vreg[DEPTH][4][VW];
 
   __device__ void init(int tok_stride, uint32_t lds, float* p, float* a) {
     lane = threadIdx.x & 63;
@@ -111,12 +123,12 @@ struct HeadPipe {
     for (int i = 0; i < NKL; ++i) {
       const int t_in = Geo::TPI * i + d_row;
       dma_off[i] = uint32_t(t_in) * tok_stride + uint32_t(d_pos ^ (t_in & Geo::SWZ)) * 16u;
+      vdma_off[i] = uint32_t(t_in) * tok_stride + uint32_t(d_pos) * 16u;
     }
 #pragma unroll
     for (int c = 0; c < NKL; ++c)
       rd_off[c] = uint32_t(m16) * Geo::RB + uint32_t((4 * c + kq) ^ (m16 & Geo::SWZ)) * 16u;
-    v_off = uint32_t(kq) * tok_stride + uint32_t(m16) * VPL * Geo::E;
-    v_round = 4u * tok_stride;
+    v_rd = uint32_t(kq) * Geo::RB + uint32_t(m16) * Geo::VB;
     lds_base = lds;
     p_lds = lds_addr(p);
     a_lds = lds_addr(a);
@@ -132,6 +144,30 @@ struct HeadPipe {
                           : u32x4{0u, 0u, 0u, 0u};
   }
 
+  // Page ids of chunk c0 of `s` (lane j: the chunk's tile min(j, nc - 1)).
+  __device__ int chunk_pages(const HeadSource& s, int c0, int nc) const {
+    const int jt = c0 + min(lane, nc - 1);
+    return s.table[(s.t_begin + (s.sub + jt * s.stride) * kTile) >> s.page_shift];
+  }
+
+  __device__ static int tiles_of(const HeadSource& s) {
+    const int n_tiles = (s.t_end - s.t_begin + kTile - 1) / kTile;
+    return n_tiles > s.sub ? (n_tiles - s.sub + s.stride - 1) / s.stride : 0;
+  }
+
+  // Start the loads of the next run()'s q operand and first page ids, so that their latency
+  // overlaps the current work; the next run() on `s` then takes them instead of loading.
+  __device__ void prefetch(const HeadSource& s, int G) {
+    const char* qrow = s.q_group + int64_t(m16) * Geo::RB;
+#pragma unroll
+    for (int c = 0; c < NKL; ++c)
+      q_pref[c] = (m16 < G) ? *reinterpret_cast<const u32x4*>(qrow + 64 * c + 16 * kq)
+                            : u32x4{0u, 0u, 0u, 0u};
+    const int n_my = tiles_of(s);
+    pv_pref = n_my > 0 ? chunk_pages(s, 0, min(kChunk, n_my)) : 0;
+    pref_ready = true;
+  }
+
   __device__ void reset() {
     m_run = neg_inf();
     l_run = 0.f;
@@ -142,8 +178,9 @@ struct HeadPipe {
     bad = false;
   }
 
-  // Issue one tile: V rows into registers, then K rows into LDS stage `st`.  An out-of-range
-  // page id reads page 0 instead (the tile is then skipped and the head's result is NaN).
+  // Issue one tile: its V rows, then its K rows, into LDS stage `st` by direct-to-LDS loads (every
+  // load of the stream writes LDS only).  An out-of-range page id reads page 0 instead (the tile
+  // is then skipped and the head's result is NaN).
   __device__ void issue(const HeadSource& s, int st, int tile, int page) {
     const int t0 = s.t_begin + tile * kTile;
     const int pg = (page >= 0 && page < s.num_pages) ? page : 0;
@@ -151,8 +188,9 @@ struct HeadPipe {
                          int64_t(t0 & ((1 << s.page_shift) - 1)) * s.tok_stride + s.head_off;
     const uint32_t kdst = lds_base + uint32_t(st * Geo::KTILE);
     const gptr vb = uniform_gptr(s.vpool + base);
+    const uint32_t vdst = lds_base + VSTAGE0 + uint32_t(st * Geo::KTILE);
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) load_words<VW>(vb + v_off + rr * v_round, vreg[st][rr]);
+    for (int i = 0; i < NKL; ++i) dma16_to_lds<kDmaPolicy>(vb + vdma_off[i], vdst + uint32_t(i * 1024));
     const gptr kb = uniform_gptr(s.kpool + base);
 #pragma unroll
     for (int i = 0; i < NKL; ++i) dma16_to_lds<kDmaPolicy>(kb + dma_off[i], kdst + uint32_t(i * 1024));
@@ -229,16 +267,28 @@ struct HeadPipe {
 #pragma unroll
         for (int e = 0; e < VPL; ++e) o[g][e] *= __uint_as_float(av[g / 4][g % 4]);
     }
-    constexpr int RPW = NR <= 2 ? 4 : 2;     // rows of p read per wait
+    constexpr int RPW = NR + VW / 4 <= 3 ? 4 : 2;   // rows of p and V read per wait
+    const uint32_t vs = lds_base + VSTAGE0 + uint32_t(st * Geo::KTILE) + v_rd;
 #pragma unroll
     for (int r0 = 0; r0 < 4; r0 += RPW) {
       u32x4 pv[RPW * NR];
+      uint32_t vw[RPW][VW];   // this lane's V words of rows 4 rr + kq
+      LdsRows<Geo::VB> vr[RPW];
 #pragma unroll
-      for (int j = 0; j < RPW; ++j)
+      for (int j = 0; j < RPW; ++j) {
+        vr[j].read(vs + uint32_t(4 * (r0 + j)) * Geo::RB);
 #pragma unroll
         for (int c = 0; c < NR; ++c)
           pv[j * NR + c] = lds_read16(p_lds + uint32_t((4 * (r0 + j) + kq) * GP + 4 * c) * 4u);
-      lds_wait_all<RPW * NR>(pv);
+      }
+      lds_wait();
+#pragma unroll
+      for (int j = 0; j < RPW; ++j) {
+        vr[j].pin();
+#pragma unroll
+        for (int c = 0; c < NR; ++c) lds_pin(pv[j * NR + c]);
+        vr[j].words(vw[j]);
+      }
 #pragma unroll
       for (int j = 0; j < RPW; ++j) {
       const int rr = r0 + j;
@@ -248,10 +298,10 @@ struct HeadPipe {
       float v[VPL];
       if constexpr (DT == DT_F32) {
 #pragma unroll
-        for (int e = 0; e < VPL; ++e) v[e] = __uint_as_float(vreg[st][rr][e]);
+        for (int e = 0; e < VPL; ++e) v[e] = __uint_as_float(vw[j][e]);
       } else {
 #pragma unroll
-        for (int e = 0; e < VPL / 2; ++e) unpack2<DT>(vreg[st][rr][e], v[2 * e], v[2 * e + 1]);
+        for (int e = 0; e < VPL / 2; ++e) unpack2<DT>(vw[j][e], v[2 * e], v[2 * e + 1]);
       }
       if (masked && t0 + 4 * rr + kq >= s.t_end) {
 #pragma unroll
@@ -279,14 +329,32 @@ struct HeadPipe {
     }
   }
 
+  // Stream all of this wave's tiles of `s`.  With has_next, the loads of the next run()'s q and
+  // first page ids (for `next`) start as the last chunk begins (see prefetch).  When prefetch() ran for `s`,
+  // its q is taken here and its first page ids are used.
+  // lockstep: every wave of the workgroup streams the same tile list (one wave per KV head); a
+  // barrier per round of DEPTH tiles then keeps the waves together, so that the rows of all
+  // heads of a token are read close in time and no wave falls behind the others.
   __device__ void run(const HeadSource& s, float scale_log2, int G) {
-    const int n_tiles = (s.t_end - s.t_begin + kTile - 1) / kTile;
-    const int n_my = n_tiles > s.sub ? (n_tiles - s.sub + s.stride - 1) / s.stride : 0;
+    run(s, scale_log2, G, s, false, false);
+  }
+  __device__ void run(const HeadSource& s, float scale_log2, int G, const HeadSource& next,
+                      bool has_next, bool lockstep) {
+    const int n_my = tiles_of(s);
+    const bool had_pref = pref_ready;
+    if (pref_ready) {
+#pragma unroll
+      for (int c = 0; c < NKL; ++c) qreg[c] = q_pref[c];
+      pref_ready = false;
+    }
     for (int c0 = 0; c0 < n_my; c0 += kChunk) {
       const int nc = min(kChunk, n_my - c0);
       // Lane j holds the page id of this wave's chunk tile min(j, nc - 1).
-      const int jt = c0 + min(lane, nc - 1);
-      const int page_vec = s.table[(s.t_begin + (s.sub + jt * s.stride) * kTile) >> s.page_shift];
+      const int page_vec = (c0 == 0 && had_pref) ? pv_pref : chunk_pages(s, c0, nc);
+      // The page ids (and anything older) have landed before the next piece's prefetch is
+      // issued, so no later wait for them can also wait for the prefetch.
+      wait_vmcnt<0>();
+      if (has_next && c0 + kChunk >= n_my) prefetch(next, G);   // the last chunk
       auto page_at = [&](int k) { return __builtin_amdgcn_readlane(page_vec, min(k, nc - 1)); };
       auto tile_at = [&](int k) { return s.sub + (c0 + min(k, nc - 1)) * s.stride; };
       auto ok = [&](int pg) { return pg >= 0 && pg < s.num_pages; };
@@ -299,6 +367,7 @@ struct HeadPipe {
       // Steady state: every stage is refilled with a tile of the chunk, so the loads issued
       // after stage d's are always those of DEPTH - 1 stages.
       for (; k + 2 * DEPTH <= nc; k += DEPTH) {
+        if (lockstep) __builtin_amdgcn_s_barrier();
 #pragma unroll
         for (int d = 0; d < DEPTH; ++d) {
           wait_vmcnt<(DEPTH - 1) * Geo::LOADS>();
@@ -320,6 +389,7 @@ struct HeadPipe {
       }
       wait_vmcnt<0>();   // nothing is in flight here; this states it for the next chunk
     }
+    if (has_next && n_my == 0) prefetch(next, G);   // no tiles of `s` for this wave
   }
 
   // Reduce the wave's state across its 4 row groups and store it at `ep` (LDS):
@@ -340,6 +410,30 @@ struct HeadPipe {
       ep[GP * D + lane] = m_run;
       ep[GP * D + GP + lane] = l_run;
       ep[GP * D + 2 * GP + lane] = bad ? 1.f : 0.f;
+    }
+  }
+
+  // Finish a head that this wave served alone, from registers: for each query head g < G of
+  // the group, emit(g, d0, vals, lse) with vals[e] = o / l for dims d0 + e (lanes 0..15 each
+  // hold VPL dims), lse in natural log.  The same arithmetic as combine_waves with one wave
+  // (its weight 2^0 is exactly 1), so the results are identical.
+  template <class Emit>
+  __device__ void finish_direct(int G, Emit emit) {
+    l_run = sum_rows4(l_run);
+#pragma unroll
+    for (int g = 0; g < GP; ++g)
+#pragma unroll
+      for (int e = 0; e < VPL; ++e) o[g][e] = sum_rows4(o[g][e]);
+#pragma unroll
+    for (int g = 0; g < GP; ++g) {
+      if (g >= G) break;
+      const float lg = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l_run), g));
+      const float mg = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m_run), g));
+      float vals[VPL];
+#pragma unroll
+      for (int e = 0; e < VPL; ++e) vals[e] = bad ? qnan() : fmaf(1.f, o[g][e], 0.f) / fmaf(1.f, lg, 0.f);
+      const float lse = bad ? qnan() : (mg + __builtin_amdgcn_logf(fmaf(1.f, lg, 0.f))) * kLn2;
+      if (lane < 16) emit(g, lane * VPL, vals, lse);
     }
   }
 };
@@ -639,73 +733,115 @@ __global__ __launch_bounds__(NW * 64) void step_kernel(const StepParams p) {
 
   HeadPipe<DT, D, GP, DEPTH> hp;
   hp.init(a.tok_stride, lds_addr(sm.w[wave]), &sm.p[wave][0][0], &sm.a[wave][0]);
-  const int row_bytes = a.hkv * Geo::RB;
-  for (; b < B && prefix[b] < hi; ++b) {
-    const int n_b = prefix[b + 1] - prefix[b];
-    if (n_b == 0) continue;
-    const int tb = max(lo, prefix[b]) - prefix[b];
-    const int te = min(hi, prefix[b + 1]) - prefix[b];
-    const int L = a.context_lens[b];
-    const int att = L + p.append;
 
-    // The workgroup holding the sequence's last tile first writes the appended rows of its
-    // heads into the pool; the barrier (which waits for the stores) orders them before the
-    // tile's loads.  No other workgroup reads that slot in this step.
-    if (p.append && te == n_b) {
-      const int page = a.page_table[int64_t(b) * a.max_pages + (L >> a.page_shift)];
-      if (page >= 0 && page < a.num_pages) {
-        const int64_t dst = int64_t(page) * a.page_stride +
-                            int64_t(L & ((1 << a.page_shift) - 1)) * a.tok_stride +
-                            int64_t(hg) * HPW * Geo::RB;
-        const int64_t srco = int64_t(b) * row_bytes + int64_t(hg) * HPW * Geo::RB;
-        for (int i = threadIdx.x; i < HPW * Geo::RB / 16; i += NW * 64) {
-          const u32x4 kv = *reinterpret_cast<const u32x4*>(static_cast<const char*>(p.k_new) + srco + 16 * i);
-          const u32x4 vv = *reinterpret_cast<const u32x4*>(static_cast<const char*>(p.v_new) + srco + 16 * i);
-          *reinterpret_cast<u32x4*>(static_cast<char*>(p.k_pool_w) + dst + 16 * i) = kv;
-          *reinterpret_cast<u32x4*>(static_cast<char*>(p.v_pool_w) + dst + 16 * i) = vv;
-        }
+  // The appended rows of every sequence whose last tile lies in this range are written first;
+  // the barrier (which waits for the stores) orders them before any load of those tiles.  No
+  // other workgroup reads those slots in this step.
+  if (p.append) {
+    const int row_bytes = a.hkv * Geo::RB;
+    for (int bb = b; bb < B && prefix[bb] < hi; ++bb) {
+      if (prefix[bb + 1] == prefix[bb] || prefix[bb + 1] > hi) continue;
+      const int L = a.context_lens[bb];
+      const int page = a.page_table[int64_t(bb) * a.max_pages + (L >> a.page_shift)];
+      if (page < 0 || page >= a.num_pages) continue;
+      const int64_t dst = int64_t(page) * a.page_stride +
+                          int64_t(L & ((1 << a.page_shift) - 1)) * a.tok_stride +
+                          int64_t(hg) * HPW * Geo::RB;
+      const int64_t srco = int64_t(bb) * row_bytes + int64_t(hg) * HPW * Geo::RB;
+      for (int i = threadIdx.x; i < HPW * Geo::RB / 16; i += NW * 64) {
+        const u32x4 kv = *reinterpret_cast<const u32x4*>(static_cast<const char*>(p.k_new) + srco + 16 * i);
+        const u32x4 vv = *reinterpret_cast<const u32x4*>(static_cast<const char*>(p.v_new) + srco + 16 * i);
+        *reinterpret_cast<u32x4*>(static_cast<char*>(p.k_pool_w) + dst + 16 * i) = kv;
+        *reinterpret_cast<u32x4*>(static_cast<char*>(p.v_pool_w) + dst + 16 * i) = vv;
       }
-      __syncthreads();
     }
+    __syncthreads();
+  }
 
-    hp.load_q(static_cast<const char*>(a.q) + (int64_t(b) * a.hq + int64_t(kvh) * G) * Geo::RB, G);
-    hp.reset();
+  // This wave's source for sequence bb: the tiles of bb in this range, for its KV head.
+  auto source = [&](int bb) {
     HeadSource src;
+    const int tb = max(lo, prefix[bb]) - prefix[bb];
+    const int te = min(hi, prefix[bb + 1]) - prefix[bb];
     src.kpool = static_cast<const char*>(a.k_pool);
     src.vpool = static_cast<const char*>(a.v_pool);
-    src.table = a.page_table + int64_t(b) * a.max_pages;
+    src.table = a.page_table + int64_t(bb) * a.max_pages;
     src.page_shift = a.page_shift;
     src.num_pages = a.num_pages;
     src.tok_stride = a.tok_stride;
     src.page_stride = a.page_stride;
     src.head_off = kvh * Geo::RB;
     src.t_begin = tb * kTile;
-    src.t_end = min(att, te * kTile);
+    src.t_end = min(a.context_lens[bb] + p.append, te * kTile);
     src.sub = wave / HPW;
     src.stride = WPH;
-    hp.run(src, a.scale_log2, G);
-    hp.to_lds(reinterpret_cast<float*>(sm.w[wave]));
-    __syncthreads();
+    src.q_group = static_cast<const char*>(a.q) + (int64_t(bb) * a.hq + int64_t(kvh) * G) * Geo::RB;
+    return src;
+  };
+  // The next sequence after bb with tiles in this range, or B.
+  auto next_seq = [&](int bb) {
+    for (++bb; bb < B && prefix[bb] < hi; ++bb)
+      if (prefix[bb + 1] > prefix[bb]) return bb;
+    return B;
+  };
 
+  // `b` holds tile `lo` (the last b with prefix[b] <= lo < T has prefix[b + 1] > lo).  Each
+  // piece's q and first page ids are loaded while the previous piece drains; the first piece's
+  // q and page ids load together.
+  HeadSource cur = source(b);
+  hp.prefetch(cur, G);
+  while (true) {
+    const int nb = next_seq(b);
+    const bool has_next = nb < B;
+    const HeadSource nxt = source(has_next ? nb : b);
+    hp.reset();
+    hp.run(cur, a.scale_log2, G, nxt, has_next, WPH == 1);
+
+    const int n_b = prefix[b + 1] - prefix[b];
+    const int tb = max(lo, prefix[b]) - prefix[b];
+    const int te = min(hi, prefix[b + 1]) - prefix[b];
     const bool whole = tb == 0 && te == n_b;   // this workgroup holds all of the sequence
     const int64_t slot = int64_t(w) + b;
-    combine_waves<D, GP, Shm::WREG>(&sm.w[0][0], HPW, WPH, G, NW * 64,
-        [&](int h_in, int g, int d, float val, float lse, bool) {
-          const int h = (hg * HPW + h_in) * G + g;
-          if (whole) {
-            store_elem<DT>(p.out, (int64_t(b) * a.hq + h) * D + d, val);
-            if (d == 0 && p.lse_out) p.lse_out[int64_t(b) * a.hq + h] = lse;
-          } else {   // device-scope stores: written through to where every XCD reads
-            dev_store(&p.ws_out[(slot * a.hq + h) * D + d], val);
-            if (d == 0) dev_store(&p.ws_lse[slot * a.hq + h], lse);
-          }
-        });
+    if (WPH == 1) {
+      // One wave per KV head: the wave finishes its head from registers, with no barrier.
+      hp.finish_direct(G, [&](int g, int d0, const float (&vals)[Geo::VPL], float lse) {
+        const int h = kvh * G + g;
+        if (whole) {
+          store_row<DT, Geo::VPL>(p.out, (int64_t(b) * a.hq + h) * D + d0, vals);
+          if (d0 == 0 && p.lse_out) p.lse_out[int64_t(b) * a.hq + h] = lse;
+        } else {   // device-scope stores: written through to where every XCD reads
+          const BufRes row = make_bufres(&p.ws_out[(slot * a.hq + h) * D], uint32_t(D * 4));
+#pragma unroll
+          for (int c = 0; c < Geo::VPL / 4; ++c)
+            dev_store16(row, uint32_t(d0 + 4 * c) * 4u,
+                        f32x4{vals[4 * c], vals[4 * c + 1], vals[4 * c + 2], vals[4 * c + 3]});
+          if (d0 == 0) dev_store(&p.ws_lse[slot * a.hq + h], lse);
+        }
+      });
+    } else {
+      hp.to_lds(reinterpret_cast<float*>(sm.w[wave]));
+      __syncthreads();
+      combine_waves<D, GP, Shm::WREG>(&sm.w[0][0], HPW, WPH, G, NW * 64,
+          [&](int h_in, int g, int d, float val, float lse, bool) {
+            const int h = (hg * HPW + h_in) * G + g;
+            if (whole) {
+              store_elem<DT>(p.out, (int64_t(b) * a.hq + h) * D + d, val);
+              if (d == 0 && p.lse_out) p.lse_out[int64_t(b) * a.hq + h] = lse;
+            } else {
+              dev_store(&p.ws_out[(slot * a.hq + h) * D + d], val);
+              if (d == 0) dev_store(&p.ws_lse[slot * a.hq + h], lse);
+            }
+          });
+      __syncthreads();   // the LDS epilogue area is reused by the next piece
+    }
 
     if (!whole) {   // a split piece starts or ends the range
       if (tb > 0) split_first = b;
       else split_last = b;
     }
-    __syncthreads();   // the LDS epilogue area is reused by the next piece
+    if (!has_next) break;
+    b = nb;
+    cur = nxt;
   }
 
   // Count the split pieces in (at most two: the range's first and last); the workgroup that
@@ -837,17 +973,16 @@ __global__ __launch_bounds__(1024) void validate_kernel(const ValidateParams p) 
 }
 
 constexpr int kWaves = 8;
-constexpr int kDepth = 2;
 
 template <int DT, int D, int GP>
 hipError_t launch_decode_t(const DecodeParams& p, bool partial, hipStream_t stream) {
   const int64_t units = int64_t(p.batch) * (p.hkv / p.heads_per_wg) * (partial ? p.max_partitions : 1);
   if (units == 0) return hipSuccess;
   if (partial)
-    hipLaunchKernelGGL((decode_kernel<DT, D, GP, kWaves, kDepth, true>), dim3(unsigned(units)),
+    hipLaunchKernelGGL((decode_kernel<DT, D, GP, kWaves, pipe_depth<DT, D>(), true>), dim3(unsigned(units)),
                        dim3(kWaves * 64), 0, stream, p);
   else
-    hipLaunchKernelGGL((decode_kernel<DT, D, GP, kWaves, kDepth, false>), dim3(unsigned(units)),
+    hipLaunchKernelGGL((decode_kernel<DT, D, GP, kWaves, pipe_depth<DT, D>(), false>), dim3(unsigned(units)),
                        dim3(kWaves * 64), 0, stream, p);
   return hipGetLastError();
 }
@@ -855,7 +990,7 @@ hipError_t launch_decode_t(const DecodeParams& p, bool partial, hipStream_t stre
 template <int DT, int D, int GP>
 hipError_t launch_step_t(const StepParams& p, hipStream_t stream) {
   const int nhg = p.a.hkv / p.a.heads_per_wg;
-  hipLaunchKernelGGL((step_kernel<DT, D, GP, kWaves, kDepth>), dim3(unsigned(p.groups * nhg)),
+  hipLaunchKernelGGL((step_kernel<DT, D, GP, kWaves, pipe_depth<DT, D>()>), dim3(unsigned(p.groups * nhg)),
                      dim3(kWaves * 64), 0, stream, p);
   return hipGetLastError();
 }
