@@ -559,19 +559,74 @@ __device__ inline int step_tiles(const StepParams& p, int b) {
   return (att + kTile - 1) / kTile;
 }
 
-// First tile of workgroup range w: the batch's T tiles are cut into `groups` equal ranges.
-__device__ inline int64_t range_start(int64_t w, int64_t T, int64_t groups) { return w * T / groups; }
+// The split of a step's work over the workgroup ranges.  Every sequence b weighs 4 units per
+// tile plus kStartUnits for its start: a range that starts a new sequence pays one pipeline
+// drain and refill, so it gets that much less streaming.  `wpre` is the exclusive prefix of the
+// weights (B + 1 entries, in LDS); the `groups` ranges cut the weighted line [0, WT) evenly,
+// and a range owns the tiles whose weighted start falls in it.  Everything depends on the
+// lengths only.
+constexpr int kStartUnits = 8;   // two tiles
 
-// Exclusive prefix sum of step_tiles over the batch into `prefix` (B + 1 entries; the last one
-// is the total).  `scan` is NT ints of scratch.  All threads of the block take part.
+struct StepSplit {
+  const int* wpre;
+  int B;
+  int64_t WT, groups;
+
+  // Tiles of the sequences before b (the exclusive tile prefix).
+  __device__ int tiles_before(int b) const { return (wpre[b] - kStartUnits * b) >> 2; }
+  __device__ int total_tiles() const { return tiles_before(B); }
+  __device__ int64_t bound(int64_t w) const { return w * WT / groups; }
+
+  // The last b in [0, B] with wpre[b] <= x.
+  __device__ int seq_at(int64_t x) const {
+    int l = 0, r = B + 1;
+    while (r - l > 1) {
+      const int m = (l + r) >> 1;
+      if (wpre[m] <= x) l = m; else r = m;
+    }
+    return l;
+  }
+  // The sequence holding tile t (tiles_before(b) <= t < tiles_before(b + 1)).
+  __device__ int seq_of_tile(int t) const {
+    int l = 0, r = B + 1;
+    while (r - l > 1) {
+      const int m = (l + r) >> 1;
+      if (tiles_before(m) <= t) l = m; else r = m;
+    }
+    return l;
+  }
+  // The first tile whose weighted start (wpre[b] + kStartUnits + 4 k for tile k of b) is >= x.
+  __device__ int first_tile_at(int64_t x) const {
+    const int b = seq_at(x);
+    if (b >= B) return total_tiles();
+    const int64_t o = x - wpre[b] - kStartUnits;
+    const int t0 = tiles_before(b);
+    const int k = o <= 0 ? 0 : int((o + 3) >> 2);
+    return min(t0 + k, tiles_before(b + 1));
+  }
+  __device__ int range_lo(int64_t w) const { return first_tile_at(bound(w)); }
+  // Within sequence b (n tiles, weighted starts base + 4 k with base = wpre[b] + kStartUnits),
+  // no search is needed: the range owning weighted position x, and how many of b's tiles range
+  // w holds.
+  __device__ int64_t range_of_pos(int64_t x) const { return ((x + 1) * groups - 1) / WT; }
+  __device__ int tiles_in(int64_t w, int64_t base, int n) const {
+    const int64_t o0 = bound(w) - base, o1 = bound(w + 1) - base;
+    const int64_t k0 = o0 <= 0 ? 0 : min<int64_t>(n, (o0 + 3) >> 2);
+    const int64_t k1 = o1 <= 0 ? 0 : min<int64_t>(n, (o1 + 3) >> 2);
+    return int(k1 - k0);
+  }
+};
+
+// Exclusive prefix sum of the weights 4 * step_tiles(b) + kStartUnits over the batch into
+// `wpre` (B + 1 entries).  `scan` is NT ints of scratch.  All threads of the block take part.
 template <int NT>
-__device__ void tile_prefix(const StepParams& p, int* prefix, int* scan) {
+__device__ void weight_prefix(const StepParams& p, int* wpre, int* scan) {
   const int B = p.a.batch;
   const int tid = threadIdx.x;
   const int seg = (B + NT - 1) / NT;
   const int lo = min(B, tid * seg), hi = min(B, lo + seg);
   int local = 0;
-  for (int b = lo; b < hi; ++b) local += step_tiles(p, b);
+  for (int b = lo; b < hi; ++b) local += 4 * step_tiles(p, b) + kStartUnits;
   scan[tid] = local;
   __syncthreads();
   for (int off = 1; off < NT; off <<= 1) {
@@ -582,28 +637,11 @@ __device__ void tile_prefix(const StepParams& p, int* prefix, int* scan) {
   }
   int run = scan[tid] - local;
   for (int b = lo; b < hi; ++b) {
-    prefix[b] = run;
-    run += step_tiles(p, b);
+    wpre[b] = run;
+    run += 4 * step_tiles(p, b) + kStartUnits;
   }
-  if (tid == NT - 1) prefix[B] = scan[NT - 1];
+  if (tid == NT - 1) wpre[B] = scan[NT - 1];
   __syncthreads();
-}
-
-// Whether workgroup range w holds tiles of [S, E), for w between the ranges of tiles S and E - 1.
-// With at least as many tiles as ranges no range is empty, and every such w qualifies.
-__device__ inline bool holds_piece(int64_t w, int64_t S, int64_t E, int64_t T, int64_t groups) {
-  return T >= groups ||
-         max(range_start(w, T, groups), S) < min(range_start(w + 1, T, groups), E);
-}
-
-// Number of workgroup ranges that hold tiles of [S, E).
-__device__ inline int pieces_of(int64_t S, int64_t E, int64_t T, int64_t groups) {
-  const int64_t w_lo = ((S + 1) * groups - 1) / T;
-  const int64_t w_hi = (E * groups - 1) / T;
-  if (T >= groups) return int(w_hi - w_lo + 1);
-  int n = 0;
-  for (int64_t w = w_lo; w <= w_hi; ++w) n += holds_piece(w, S, E, T, groups);
-  return n;
 }
 
 // Merge of sequence b's pieces for the NH query heads of head group hg:
@@ -611,13 +649,19 @@ __device__ inline int pieces_of(int64_t S, int64_t E, int64_t T, int64_t groups)
 // Each thread takes two float4 columns and issues the loads of up to kMU pieces of both at once
 // (16-byte device-scope loads of the partial rows, one device-scope load of each log-sum-exp),
 // carrying a running maximum from one group of pieces to the next.
+// `flags` (NT ints of LDS) receives which of the first NT candidate ranges hold a piece; all
+// threads of the block take part.
 template <int DT, int D, int NT>
-__device__ void step_merge(const StepParams& p, int b, int hg, int NH, int64_t S, int64_t E,
-                           int64_t T) {
+__device__ void step_merge(const StepParams& p, const StepSplit& sp, int b, int hg, int NH, int S,
+                           int E, int* flags) {
   constexpr int kMU = 8, kCols = 2;
   const DecodeParams& a = p.a;
-  const int64_t w_lo = ((S + 1) * p.groups - 1) / T;
-  const int npc = int((E * p.groups - 1) / T - w_lo + 1);   // candidate ranges
+  const int n = E - S;
+  const int64_t base = sp.wpre[b] + kStartUnits;   // weighted start of the sequence's first tile
+  const int64_t w_lo = sp.range_of_pos(base);
+  const int npc = int(sp.range_of_pos(base + 4 * int64_t(n - 1)) - w_lo + 1);   // candidate ranges
+  if (threadIdx.x < min(npc, NT)) flags[threadIdx.x] = sp.tiles_in(w_lo + threadIdx.x, base, n) > 0;
+  __syncthreads();
   const int ncol = NH * (D / 4);
   // Byte offsets below are relative to the first candidate's partial rows.
   const int64_t row0 = (w_lo + b) * a.hq;
@@ -640,7 +684,8 @@ __device__ void step_merge(const StepParams& p, int b, int hg, int NH, int64_t S
       f32x4 vs[kCols][kMU];
 #pragma unroll
       for (int u = 0; u < kMU; ++u) {
-        const bool ok = k0 + u < npc && holds_piece(w_lo + k0 + u, S, E, T, p.groups);
+        const int k = k0 + u;
+        const bool ok = k < npc && (k < NT ? flags[k] != 0 : sp.tiles_in(w_lo + k, base, n) > 0);
 #pragma unroll
         for (int k = 0; k < kCols; ++k) {
           const int64_t row = int64_t(k0 + u) * a.hq + h[k];
@@ -678,6 +723,7 @@ __device__ void step_merge(const StepParams& p, int b, int hg, int NH, int64_t S
         p.lse_out[int64_t(b) * a.hq + h[k]] = m[k] + __builtin_amdgcn_logf(l[k]) * kLn2;
     }
   }
+  __syncthreads();   // `flags` may be rewritten next
 }
 
 template <int DT, int D, int GP, int NW, int DEPTH>
@@ -686,7 +732,7 @@ __global__ __launch_bounds__(NW * 64) void step_kernel(const StepParams p) {
   using Shm = DecodeShared<DT, D, GP, NW, DEPTH>;
   static_assert((DEPTH - 1) * Geo::LOADS < 64, "vmcnt range");
   __shared__ Shm sm;
-  __shared__ int prefix[kMaxStepBatch + 1];
+  __shared__ int wpre[kMaxStepBatch + 1];
   __shared__ int scan[NW * 64];
 
   const DecodeParams& a = p.a;
@@ -701,14 +747,16 @@ __global__ __launch_bounds__(NW * 64) void step_kernel(const StepParams p) {
 
   __shared__ int merging[2];
   int split_first = -1, split_last = -1;   // sequences whose piece here is split
+  int first_tiles = 0, last_tiles = 0;      // ... and the tiles of those pieces
 
-  tile_prefix<NW * 64>(p, prefix, scan);
+  weight_prefix<NW * 64>(p, wpre, scan);
   const int B = a.batch;
-  const int64_t T = prefix[B];
+  const StepSplit sp{wpre, B, wpre[B], p.groups};
+  auto prefix = [&](int x) { return sp.tiles_before(x); };   // tiles of the sequences before x
   // Rows without tiles (padding, or longer than the page table can address): 0 / NaN outputs,
   // written by one workgroup each.
   for (int bb = blockIdx.x; bb < B; bb += gridDim.x) {
-    if (prefix[bb + 1] != prefix[bb]) continue;
+    if (prefix(bb + 1) != prefix(bb)) continue;
     const bool pad = a.context_lens[bb] < 0 || a.context_lens[bb] + p.append <= 0;
     for (int i = threadIdx.x; i < a.hq * D; i += NW * 64)
       store_elem<DT>(p.out, int64_t(bb) * a.hq * D + i, pad ? 0.f : qnan());
@@ -716,20 +764,11 @@ __global__ __launch_bounds__(NW * 64) void step_kernel(const StepParams p) {
       for (int h = threadIdx.x; h < a.hq; h += NW * 64)
         p.lse_out[int64_t(bb) * a.hq + h] = pad ? neg_inf() : qnan();
   }
-  const int lo = int(range_start(w, T, p.groups));
-  const int hi = int(range_start(w + 1, T, p.groups));
+  const int lo = sp.range_lo(w);
+  const int hi = sp.range_lo(w + 1);
   if (lo >= hi) return;
 
-  // First sequence with tiles at or after `lo`.
-  int b = 0;
-  {
-    int l = 0, r = B;   // find the last b with prefix[b] <= lo
-    while (r - l > 1) {
-      const int m = (l + r) / 2;
-      if (prefix[m] <= lo) l = m; else r = m;
-    }
-    b = l;
-  }
+  int b = sp.seq_of_tile(lo);   // the sequence holding tile `lo`
 
   HeadPipe<DT, D, GP, DEPTH> hp;
   hp.init(a.tok_stride, lds_addr(sm.w[wave]), &sm.p[wave][0][0], &sm.a[wave][0]);
@@ -739,8 +778,8 @@ __global__ __launch_bounds__(NW * 64) void step_kernel(const StepParams p) {
   // other workgroup reads those slots in this step.
   if (p.append) {
     const int row_bytes = a.hkv * Geo::RB;
-    for (int bb = b; bb < B && prefix[bb] < hi; ++bb) {
-      if (prefix[bb + 1] == prefix[bb] || prefix[bb + 1] > hi) continue;
+    for (int bb = b; bb < B && prefix(bb) < hi; ++bb) {
+      if (prefix(bb + 1) == prefix(bb) || prefix(bb + 1) > hi) continue;
       const int L = a.context_lens[bb];
       const int page = a.page_table[int64_t(bb) * a.max_pages + (L >> a.page_shift)];
       if (page < 0 || page >= a.num_pages) continue;
@@ -761,8 +800,8 @@ __global__ __launch_bounds__(NW * 64) void step_kernel(const StepParams p) {
   // This wave's source for sequence bb: the tiles of bb in this range, for its KV head.
   auto source = [&](int bb) {
     HeadSource src;
-    const int tb = max(lo, prefix[bb]) - prefix[bb];
-    const int te = min(hi, prefix[bb + 1]) - prefix[bb];
+    const int tb = max(lo, prefix(bb)) - prefix(bb);
+    const int te = min(hi, prefix(bb + 1)) - prefix(bb);
     src.kpool = static_cast<const char*>(a.k_pool);
     src.vpool = static_cast<const char*>(a.v_pool);
     src.table = a.page_table + int64_t(bb) * a.max_pages;
@@ -780,14 +819,13 @@ __global__ __launch_bounds__(NW * 64) void step_kernel(const StepParams p) {
   };
   // The next sequence after bb with tiles in this range, or B.
   auto next_seq = [&](int bb) {
-    for (++bb; bb < B && prefix[bb] < hi; ++bb)
-      if (prefix[bb + 1] > prefix[bb]) return bb;
+    for (++bb; bb < B && prefix(bb) < hi; ++bb)
+      if (prefix(bb + 1) > prefix(bb)) return bb;
     return B;
   };
 
-  // `b` holds tile `lo` (the last b with prefix[b] <= lo < T has prefix[b + 1] > lo).  Each
-  // piece's q and first page ids are loaded while the previous piece drains; the first piece's
-  // q and page ids load together.
+  // Each piece's q and first page ids are loaded while the previous piece drains; the first
+  // piece's q and page ids load together.
   HeadSource cur = source(b);
   hp.prefetch(cur, G);
   while (true) {
@@ -797,9 +835,9 @@ __global__ __launch_bounds__(NW * 64) void step_kernel(const StepParams p) {
     hp.reset();
     hp.run(cur, a.scale_log2, G, nxt, has_next, WPH == 1);
 
-    const int n_b = prefix[b + 1] - prefix[b];
-    const int tb = max(lo, prefix[b]) - prefix[b];
-    const int te = min(hi, prefix[b + 1]) - prefix[b];
+    const int n_b = prefix(b + 1) - prefix(b);
+    const int tb = max(lo, prefix(b)) - prefix(b);
+    const int te = min(hi, prefix(b + 1)) - prefix(b);
     const bool whole = tb == 0 && te == n_b;   // this workgroup holds all of the sequence
     const int64_t slot = int64_t(w) + b;
     if (WPH == 1) {
@@ -836,16 +874,21 @@ __global__ __launch_bounds__(NW * 64) void step_kernel(const StepParams p) {
     }
 
     if (!whole) {   // a split piece starts or ends the range
-      if (tb > 0) split_first = b;
-      else split_last = b;
+      if (tb > 0) {
+        split_first = b;
+        first_tiles = te - tb;
+      } else {
+        split_last = b;
+        last_tiles = te - tb;
+      }
     }
     if (!has_next) break;
     b = nb;
     cur = nxt;
   }
 
-  // Count the split pieces in (at most two: the range's first and last); the workgroup that
-  // brings in a sequence's last piece merges all of its pieces.  This is deferred to the end of
+  // Count the split pieces' tiles in (at most two pieces: the range's first and last); the
+  // workgroup that brings a sequence's count to its number of tiles merges all of its pieces.  This is deferred to the end of
   // the range so that no workgroup stalls between pieces.  The partials were written, and are
   // read, with device-scope accesses, which are coherent across the XCDs (each has its own L2)
   // without an L2 write-back or invalidate: each thread waits until its stores are complete,
@@ -856,12 +899,12 @@ __global__ __launch_bounds__(NW * 64) void step_kernel(const StepParams p) {
   __syncthreads();
   if (threadIdx.x < 2) {
     const int sb = threadIdx.x == 0 ? split_first : split_last;
+    const int tiles = threadIdx.x == 0 ? first_tiles : last_tiles;
     int last = 0;
     if (sb >= 0) {
-      const int need = pieces_of(prefix[sb], prefix[sb + 1], T, p.groups);
-      const int old = __hip_atomic_fetch_add(&p.ws_count[int64_t(sb) * nhg + hg], 1,
+      const int old = __hip_atomic_fetch_add(&p.ws_count[int64_t(sb) * nhg + hg], tiles,
                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      last = old == need - 1;
+      last = old + tiles == prefix(sb + 1) - prefix(sb);
     }
     merging[threadIdx.x] = last;
   }
@@ -869,7 +912,7 @@ __global__ __launch_bounds__(NW * 64) void step_kernel(const StepParams p) {
   for (int i = 0; i < 2; ++i) {
     const int sb = i == 0 ? split_first : split_last;
     if (!merging[i]) continue;
-    step_merge<DT, D, NW * 64>(p, sb, hg, HPW * a.group, prefix[sb], prefix[sb + 1], T);
+    step_merge<DT, D, NW * 64>(p, sp, sb, hg, HPW * a.group, prefix(sb), prefix(sb + 1), scan);
     if (threadIdx.x == 0)   // ready for the next call
       __hip_atomic_store(&p.ws_count[int64_t(sb) * nhg + hg], 0, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);

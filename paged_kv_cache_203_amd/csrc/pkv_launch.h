@@ -29,8 +29,9 @@ struct DecodeParams {
 
 // Balanced decode step: `a` carries the attention arguments (heads_per_wg set; the partition
 // fields are unused).  Workspace (laid out by step_workspace): per-(sequence, head group)
-// arrival counters ws_count (zero before the first call; every call leaves them at zero),
-// piece partials ws_out [(groups + B) * Hq * D] and ws_lse [(groups + B) * Hq].
+// counters of the tiles whose pieces have arrived, ws_count (zero before the first call; every
+// call leaves them at zero), piece partials ws_out [(groups + B) * Hq * D] and ws_lse
+// [(groups + B) * Hq].
 struct StepParams {
   DecodeParams a;
   const void* k_new;     // null: no append
