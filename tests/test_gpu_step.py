@@ -201,3 +201,28 @@ def test_step_repeated_calls_bitwise_stable(pkv):
         else:
             for j in range(2):
                 assert torch.equal(outs[j].view(torch.int16), first[j].view(torch.int16)), (rep, j)
+
+
+STEP_SHAPES = [  # (Hkv, G, D, PS, dtype, max length): one wave per KV head (Hkv % 8 == 0) or
+    # several (Hkv 1, 2, 4), two head groups per range (Hkv 16), every padded group size, both
+    # head sizes, fp32 with head_dim 128 (one tile in flight), pages of 16 to 256 tokens
+    (2, 1, 128, 16, "bf16", 700), (2, 3, 64, 16, "bf16", 300), (8, 2, 128, 64, "f16", 2500),
+    (16, 1, 128, 16, "bf16", 1200), (8, 16, 64, 256, "f16", 1500), (4, 5, 64, 32, "f32", 900),
+    (8, 2, 128, 128, "f32", 1000), (1, 4, 128, 16, "bf16", 4000), (8, 7, 128, 32, "bf16", 3000),
+]
+
+
+@pytest.mark.parametrize("Hkv,G,D,PS,dtype,Lmax", STEP_SHAPES)
+def test_step_shapes(pkv, Hkv, G, D, PS, dtype, Lmax):
+    import dataclasses
+    cfg = dataclasses.replace(W.config(4), name=f"step-H{Hkv}-G{G}-D{D}-PS{PS}-{dtype}", batch=6,
+                              num_q_heads=Hkv * G, num_kv_heads=Hkv, head_dim=D, page_size=PS,
+                              dtype=dtype, lengths=("uniform", 1, Lmax), append=True)
+    w = W.make_workload(cfg)
+    log(f"case {cfg.name} lens={w.context_lens.tolist()}")
+    d, out, lse, pools = run_step(pkv, w, True, lse=True)
+    assert np.array_equal(to_numpy_storage(d.k_pool, w.dtype).view(np.uint8), pools[0].view(np.uint8))
+    assert np.array_equal(to_numpy_storage(d.v_pool, w.dtype).view(np.uint8), pools[1].view(np.uint8))
+    ref, ref_lse = oracle_for(w, pools)
+    assert_parity(to_f64(out), ref, dtype, cfg.name)
+    assert np.abs(lse.double().cpu().numpy() - ref_lse).max() <= 1e-4
