@@ -46,7 +46,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=2, help="workload index (default: 2)")
-    ap.add_argument("--path", choices=["step", "split", "single"], default="step")
+    ap.add_argument("--path", choices=["step", "split", "single", "cascade"], default="step",
+                    help="cascade: shared-prefix decode (prefix-shared workloads only)")
     ap.add_argument("--partition-tokens", type=int, default=None)
     ap.add_argument("--replicas", type=int, default=None,
                     help="pool replicas rotated per step (default: enough for >= 2 GB)")
@@ -78,6 +79,16 @@ def step_bytes(w, partition_tokens, path):
         step = kv + q + out + table + append + 2 * partials + B * 4
     elif path == "step":
         kernel = step = kv + q + out + table + append   # one launch does all of it
+    elif path == "cascade":
+        # The shared prefix pages are read once: unique KV bytes, plus every partition's partial
+        # written and read back by the merge.
+        P = w.shared_pages * PS
+        uniq = (P + int(np.maximum(L - P, 0).sum())) * 2 * Hkv * D * e
+        nparts = -(-L // partition_tokens)
+        partials = int(nparts.sum()) * Hq * (D + 1) * 4
+        kernel = uniq + q + out + table + 2 * partials + B * 4
+        step = kernel + append
+        return dict(kv=uniq, step=step, kernel=kernel)
     else:
         kernel = kv + q + out + table
         step = kernel + append
@@ -205,7 +216,9 @@ def main():
         k_new = fill_normal((B, Hkv, D), cfg.dtype, w.seed, STREAM_KNEW)
         v_new = fill_normal((B, Hkv, D), cfg.dtype, w.seed, STREAM_VNEW)
         append_lens = (w.context_lens - 1).astype(np.int32)
-    P = args.partition_tokens or cfg.partition_tokens or 512
+    if args.path == "cascade" and cfg.lengths[0] != "prefix":
+        raise SystemExit("--path cascade needs a prefix-shared workload")
+    P = args.partition_tokens or cfg.partition_tokens or (256 if args.path == "cascade" else 512)
     log(f"workload {cfg.name}: generated in {time.perf_counter() - t_gen:.1f}s, "
         f"{w.logical_tokens()} live tokens, pool {w.k_pool.shape}")
 
@@ -234,6 +247,9 @@ def main():
     scale = float(w.scale)
     stream = torch.cuda.current_stream(dev)
 
+    prefix_tokens = w.shared_pages * PS
+    prefix_pages = torch.from_numpy(np.ascontiguousarray(
+        w.page_table[int(np.argmax(w.context_lens > 0)), :w.shared_pages])).to(dev)
     ws = None
     if args.path == "step":
         ws = torch.zeros(pkv.decode_step_workspace_bytes(q, k0, table), dtype=torch.uint8, device=dev)
@@ -251,7 +267,12 @@ def main():
         pkv.paged_kv_append(kn, vn, kp, vp, table, alens)
         if ev is not None:
             ev[0].record(stream)
-        if args.path == "split":
+        if args.path == "cascade":
+            pkv.paged_decode_cascade(q, kp, vp, prefix_pages, prefix_tokens, table, lens, P, scale,
+                                     out=out, partial_out=po, partial_lse=pl)
+            if ev is not None:
+                ev[1].record(stream)
+        elif args.path == "split":
             pkv.paged_decode_attention_partial(q, kp, vp, table, lens, P, scale, po, pl, maxp)
             if ev is not None:
                 ev[1].record(stream)
@@ -292,6 +313,7 @@ def main():
         log(f"CPU oracle: {cpu['s_per_step']:.3f} s/step, {cpu['value']} GB/s")
 
     kernel_name = {"split": "decode_kernel (split-KV partial attention)",
+                   "cascade": "pkv_paged_decode_cascade (prefix on MFMA + suffix partitions + merge)",
                    "single": "decode_kernel (single pass)",
                    "step": "step_kernel (pkv_paged_decode_step: append + balanced attention + merge)"}[args.path]
     line = {
@@ -310,11 +332,12 @@ def main():
         "config": {
             "workload": cfg.name,
             "description": {"split": "append + split-KV paged decode attention + LSE merge",
+                            "cascade": "append + shared-prefix decode: prefix on the matrix cores, suffix partitions, LSE merge",
                             "single": "append + single-pass paged decode attention",
                             "step": "one decode step in one launch: append, balanced split-KV attention, LSE merge"}[args.path],
             "batch": B, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D, "page_size": PS,
             "context_lens": list(cfg.lengths), "seed": w.seed, "live_tokens": w.logical_tokens(),
-            "partition_tokens": P if args.path == "split" else None, "path": args.path,
+            "partition_tokens": P if args.path in ("split", "cascade") else None, "path": args.path,
             "pool_replicas": R,
             "step_bytes": nb["step"], "kv_bytes": nb["kv"],
         },

@@ -124,6 +124,40 @@ int pkv_lse_merge(const float* partial_out, const float* partial_lse,
                   const int32_t* context_lens, int32_t partition_tokens, int32_t max_partitions,
                   void* out, float* lse_out, const pkv_shape* shape, void* stream);
 
+/* Shared-prefix (cascade) decode: paged decode attention for a batch whose sequences all begin
+ * with the same prefix_tokens tokens, stored once in the pool.
+ *
+ * Token t < prefix_tokens of every sequence is slot t % PS of page prefix_pages[t / PS]
+ * (prefix_pages holds prefix_tokens / PS page ids; the page tables' first prefix_tokens / PS
+ * entries are not read); tokens t >= prefix_tokens are found through page_table as usual.  The
+ * result is that of pkv_paged_decode_attention over L_b = context_lens[b] tokens (rows with
+ * L_b < prefix_tokens attend to their first L_b prefix tokens only), computed as three launches
+ * on `stream`:
+ *   1. the prefix partitions p < prefix_tokens / P (P = partition_tokens): for each KV head, the
+ *      query rows of all sequences (B x G rows) attend to the prefix as one dense product on the
+ *      matrix cores, so each prefix page is read once per 128 query rows, not once per sequence;
+ *   2. the remaining partitions, as pkv_paged_decode_attention_partial computes them;
+ *   3. the merge of all ceil(L_b / P) partitions, as pkv_lse_merge.
+ * partial_out / partial_lse are the caller's workspace in the split layout (their contents after
+ * the call are the partitions' partials); out and lse_out (may be NULL) are as for
+ * pkv_lse_merge.  This follows the shared prefix-page reuse of the TorchInferno page ("Design
+ * Coverage") and the Infinity docs' direction of sharing one block store across related
+ * requests ("Short shared prefix qualification"); the split into prefix and suffix partitions
+ * merged by log-sum-exp is the cascade form of the split-KV decode.
+ *
+ * Requirements: dtype bf16 or f16 (else PKV_EUNSUPPORTED); partition_tokens a multiple of 64 and
+ * of page_size, with partition_tokens / page_size <= 512; prefix_tokens a multiple of
+ * partition_tokens in [0, max_pages_per_seq * page_size]; max_partitions as for the split call.
+ * Prefix page ids outside [0, num_pages) give NaN outputs for the rows that reach them.  The
+ * partials' bits depend only on the sequence's own tokens and P; the prefix partials are not
+ * bitwise those of the split call (a different summation order), but agree to rounding. */
+int pkv_paged_decode_cascade(const void* q, const void* k_pool, const void* v_pool,
+                             const int32_t* prefix_pages, int32_t prefix_tokens,
+                             const int32_t* page_table, const int32_t* context_lens, float scale,
+                             int32_t partition_tokens, float* partial_out, float* partial_lse,
+                             int32_t max_partitions, void* out, float* lse_out,
+                             const pkv_shape* shape, void* stream);
+
 /* Paged KV append: the new token's key and value rows of every sequence are copied, bit for
  * bit, into the pools at logical position L_b = context_lens[b] (the pre-append length), i.e.
  * slot L_b % PS of page page_table[b][L_b / PS].  Rows with context_lens[b] < 0 are padding and

@@ -54,6 +54,9 @@ _SIGNATURES = {
     "pkv_paged_decode_step": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float,
                                              _vp, ctypes.c_size_t, _vp, _vp,
                                              ctypes.POINTER(PkvShape), _vp]),
+    "pkv_paged_decode_cascade": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _vp, _vp, ctypes.c_float,
+                                                _i32, _vp, _vp, _i32, _vp, _vp,
+                                                ctypes.POINTER(PkvShape), _vp]),
     "pkv_decode_step_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(PkvShape)]),
     "pkv_partial_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(PkvShape), _i32]),
     "pkv_last_error": (ctypes.c_char_p, []),
@@ -246,6 +249,46 @@ def paged_decode_attention_split(q, k_pool, v_pool, page_table, context_lens,
     return lse_merge(po, pl, context_lens, partition_tokens, k_pool.shape[1],
                      page_table.shape[1], out=out if out is not None else _torch().empty_like(q),
                      lse_out=lse_out)
+
+
+def paged_decode_cascade(q, k_pool, v_pool, prefix_pages, prefix_tokens: int, page_table,
+                         context_lens, partition_tokens: int, scale: Optional[float] = None,
+                         out=None, lse_out=None, partial_out=None, partial_lse=None):
+    """Shared-prefix decode: tokens ``t < prefix_tokens`` of every sequence are read from
+    ``prefix_pages`` (int32 ``[prefix_tokens / page_size]``), the rest through ``page_table``.
+    Returns ``out [B, Hq, D]``; the partials (allocated when not given) are the workspace."""
+    torch = _torch()
+    s = _attention_shape(q, k_pool, v_pool, page_table, context_lens)
+    _require(prefix_pages, "prefix_pages", dtype=torch.int32, ndim=1, device=q.device)
+    if prefix_pages.shape[0] * s.page_size < prefix_tokens:
+        raise ValueError("prefix_pages holds fewer than prefix_tokens / page_size ids")
+    max_partitions = (partial_lse.shape[2] if partial_lse is not None else
+                      partitions_needed(s.page_size, s.max_pages_per_seq, partition_tokens))
+    if partial_out is None:
+        partial_out = torch.empty((s.batch, s.num_q_heads, max_partitions, s.head_dim),
+                                  dtype=torch.float32, device=q.device)
+    if partial_lse is None:
+        partial_lse = torch.empty((s.batch, s.num_q_heads, max_partitions),
+                                  dtype=torch.float32, device=q.device)
+    _require(partial_out, "partial_out", dtype=torch.float32, ndim=4, device=q.device)
+    _require(partial_lse, "partial_lse", dtype=torch.float32, ndim=3, device=q.device)
+    if (tuple(partial_out.shape) != (s.batch, s.num_q_heads, max_partitions, s.head_dim)
+            or tuple(partial_lse.shape) != (s.batch, s.num_q_heads, max_partitions)):
+        raise ValueError("partial buffers have the wrong shape")
+    if out is None:
+        out = torch.empty_like(q)
+    _require(out, "out", dtype=q.dtype, ndim=3, device=q.device)
+    lse_ptr = None
+    if lse_out is not None:
+        _require(lse_out, "lse_out", dtype=torch.float32, ndim=2, device=q.device)
+        lse_ptr = lse_out.data_ptr()
+    scale = _default_scale(s.head_dim) if scale is None else float(scale)
+    _check(lib.pkv_paged_decode_cascade(
+        q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), prefix_pages.data_ptr(),
+        int(prefix_tokens), page_table.data_ptr(), context_lens.data_ptr(), scale,
+        int(partition_tokens), partial_out.data_ptr(), partial_lse.data_ptr(),
+        int(max_partitions), out.data_ptr(), lse_ptr, ctypes.byref(s), _stream(q.device)))
+    return out
 
 
 def decode_step_workspace_bytes(q, k_pool, page_table) -> int:

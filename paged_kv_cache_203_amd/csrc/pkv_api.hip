@@ -131,6 +131,72 @@ int pkv_paged_decode_attention_partial(const void* q, const void* k_pool, const 
                        "pkv_paged_decode_attention_partial");
 }
 
+int pkv_paged_decode_cascade(const void* q, const void* k_pool, const void* v_pool,
+                             const int32_t* prefix_pages, int32_t prefix_tokens,
+                             const int32_t* page_table, const int32_t* context_lens, float scale,
+                             int32_t partition_tokens, float* partial_out, float* partial_lse,
+                             int32_t max_partitions, void* out, float* lse_out,
+                             const pkv_shape* shape, void* stream) {
+  std::string msg;
+  const int rc = pkv::check_cascade(q, k_pool, v_pool, prefix_pages, prefix_tokens, page_table,
+                                    context_lens, scale, partition_tokens, partial_out,
+                                    partial_lse, max_partitions, out, lse_out, shape, msg);
+  if (rc) return set_error(rc, "pkv_paged_decode_cascade: " + msg);
+  if (shape->batch == 0) return PKV_OK;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  pkv::DecodeParams d = decode_params(q, k_pool, v_pool, page_table, context_lens, scale, *shape);
+  (void)hipGetLastError();
+
+  pkv::PrefixParams pp{};
+  pp.q = q;
+  pp.k_pool = k_pool;
+  pp.v_pool = v_pool;
+  pp.prefix_pages = prefix_pages;
+  pp.context_lens = context_lens;
+  pp.partial_out = partial_out;
+  pp.partial_lse = partial_lse;
+  pp.scale_log2 = d.scale_log2;
+  pp.batch = d.batch;
+  pp.hq = d.hq;
+  pp.hkv = d.hkv;
+  pp.group = d.group;
+  pp.num_pages = d.num_pages;
+  pp.page_shift = d.page_shift;
+  pp.capacity = d.capacity;
+  pp.prefix_tokens = prefix_tokens;
+  pp.partition_tokens = partition_tokens;
+  pp.max_partitions = max_partitions;
+  pp.tok_stride = d.tok_stride;
+  pp.page_stride = d.page_stride;
+  int r = launch_status(pkv::launch_prefix(pp, shape->dtype, shape->head_dim, st),
+                        "pkv_paged_decode_cascade (prefix)");
+  if (r) return r;
+
+  d.partial_out = partial_out;
+  d.partial_lse = partial_lse;
+  d.partition_tokens = partition_tokens;
+  d.max_partitions = max_partitions;
+  d.part_begin = prefix_tokens / partition_tokens;
+  d.heads_per_wg = heads_per_workgroup(d.hkv);
+  r = launch_status(pkv::launch_decode(d, shape->dtype, shape->head_dim, group_pad(d.group), true, st),
+                    "pkv_paged_decode_cascade (suffix)");
+  if (r) return r;
+
+  pkv::MergeParams m{};
+  m.partial_out = partial_out;
+  m.partial_lse = partial_lse;
+  m.context_lens = context_lens;
+  m.out = out;
+  m.lse_out = lse_out;
+  m.batch = shape->batch;
+  m.hq = shape->num_q_heads;
+  m.partition_tokens = partition_tokens;
+  m.max_partitions = max_partitions;
+  m.capacity = d.capacity;
+  return launch_status(pkv::launch_merge(m, shape->dtype, shape->head_dim, st),
+                       "pkv_paged_decode_cascade (merge)");
+}
+
 size_t pkv_decode_step_workspace_bytes(const pkv_shape* shape) {
   std::string msg;
   if (pkv::check_shape(shape, msg) != PKV_OK) return 0;

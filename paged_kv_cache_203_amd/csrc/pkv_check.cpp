@@ -176,6 +176,50 @@ int check_merge(const float* partial_out, const float* partial_lse, const int32_
   return PKV_OK;
 }
 
+int check_cascade(const void* q, const void* k_pool, const void* v_pool,
+                  const int32_t* prefix_pages, int32_t prefix_tokens, const int32_t* page_table,
+                  const int32_t* context_lens, float scale, int32_t partition_tokens,
+                  const float* partial_out, const float* partial_lse, int32_t max_partitions,
+                  const void* out, const float* lse_out, const pkv_shape* s, std::string& msg) {
+  int rc = check_partial(q, k_pool, v_pool, page_table, context_lens, scale, partition_tokens,
+                         partial_out, partial_lse, max_partitions, s, msg);
+  if (rc) return rc;
+  if (s->dtype != PKV_BF16 && s->dtype != PKV_F16)
+    return fail(msg, PKV_EUNSUPPORTED, "the shared-prefix path supports bf16 and f16 only");
+  if (partition_tokens % kPrefixBlock != 0)
+    return fail(msg, PKV_EUNSUPPORTED, "partition_tokens must be a multiple of 64");
+  if (partition_tokens / s->page_size > kMaxPrefixPageIds)
+    return fail(msg, PKV_EUNSUPPORTED, "partition_tokens / page_size must be <= 512");
+  const int64_t capacity = int64_t(s->max_pages_per_seq) * s->page_size;
+  if (prefix_tokens < 0 || prefix_tokens % partition_tokens != 0 || prefix_tokens > capacity)
+    return fail(msg, PKV_EINVAL,
+                "prefix_tokens must be a multiple of partition_tokens in [0, max_pages_per_seq * page_size]");
+  if (s->batch == 0) return PKV_OK;
+  if (prefix_tokens > 0 && (!prefix_pages || !aligned(prefix_pages, 4)))
+    return fail(msg, PKV_EINVAL, "prefix_pages must be non-NULL and 4-byte aligned");
+  if (!out) return fail(msg, PKV_EINVAL, "out must be non-NULL");
+  if (!aligned(out, 16)) return fail(msg, PKV_EUNSUPPORTED, "out must be 16-byte aligned");
+  if (lse_out && !aligned(lse_out, 4)) return fail(msg, PKV_EINVAL, "lse_out must be 4-byte aligned");
+  const Extents x = extents(*s);
+  const uint64_t rows = uint64_t(s->batch) * s->num_q_heads * uint64_t(max_partitions);
+  const uint64_t po = rows * s->head_dim * 4, pl = rows * 4;
+  const uint64_t lo = uint64_t(s->batch) * s->num_q_heads * 4;
+  const uint64_t pp = uint64_t(prefix_tokens / s->page_size) * 4;
+  if (overlaps(partial_out, po, prefix_pages, pp) || overlaps(partial_lse, pl, prefix_pages, pp))
+    return fail(msg, PKV_EINVAL, "partial buffers overlap prefix_pages");
+  const void* ins[7] = {q, k_pool, v_pool, page_table, context_lens, partial_out, partial_lse};
+  const uint64_t ins_n[7] = {x.q, x.pool, x.pool, x.table, x.lens, po, pl};
+  for (int i = 0; i < 7; ++i) {
+    if (overlaps(out, x.out, ins[i], ins_n[i])) return fail(msg, PKV_EINVAL, "out overlaps another buffer");
+    if (lse_out && overlaps(lse_out, lo, ins[i], ins_n[i]))
+      return fail(msg, PKV_EINVAL, "lse_out overlaps another buffer");
+  }
+  if (overlaps(out, x.out, prefix_pages, pp) || (lse_out && overlaps(lse_out, lo, prefix_pages, pp)))
+    return fail(msg, PKV_EINVAL, "an output overlaps prefix_pages");
+  if (lse_out && overlaps(lse_out, lo, out, x.out)) return fail(msg, PKV_EINVAL, "lse_out overlaps out");
+  return PKV_OK;
+}
+
 int check_append(const void* k_new, const void* v_new, const void* k_pool, const void* v_pool,
                  const int32_t* page_table, const int32_t* context_lens, const pkv_shape* s,
                  std::string& msg) {

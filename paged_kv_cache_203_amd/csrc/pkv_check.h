@@ -51,6 +51,17 @@ int check_append(const void* k_new, const void* v_new, const void* k_pool, const
 constexpr int kMaxStepBatch = 4096;
 constexpr int kMaxStepHeads = 1024;
 
+// Shared-prefix decode: most prefix page ids one partition may span (they are staged in LDS), and
+// the token block the partition length must be a multiple of.
+constexpr int kMaxPrefixPageIds = 512;
+constexpr int kPrefixBlock = 64;
+
+int check_cascade(const void* q, const void* k_pool, const void* v_pool,
+                  const int32_t* prefix_pages, int32_t prefix_tokens, const int32_t* page_table,
+                  const int32_t* context_lens, float scale, int32_t partition_tokens,
+                  const float* partial_out, const float* partial_lse, int32_t max_partitions,
+                  const void* out, const float* lse_out, const pkv_shape* s, std::string& msg);
+
 // Workspace layout of the balanced decode step for `groups` workgroup ranges (all offsets
 // 256-byte aligned).  The arrival counters (one per sequence and group of heads_per_wg KV heads)
 // come first and are sized for kMaxStepBatch sequences, so their place does not move with the

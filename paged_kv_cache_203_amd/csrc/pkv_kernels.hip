@@ -491,7 +491,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams p) {
   const int hg = id % nhg;
   id /= nhg;
   const int b = id % p.batch;
-  const int part = PARTIAL ? id / p.batch : 0;
+  const int part = PARTIAL ? p.part_begin + id / p.batch : 0;
   const int kvh = hg * HPW + wave % HPW;
 
   const int L = p.context_lens[b];
@@ -1019,8 +1019,9 @@ constexpr int kWaves = 8;
 
 template <int DT, int D, int GP>
 hipError_t launch_decode_t(const DecodeParams& p, bool partial, hipStream_t stream) {
-  const int64_t units = int64_t(p.batch) * (p.hkv / p.heads_per_wg) * (partial ? p.max_partitions : 1);
-  if (units == 0) return hipSuccess;
+  const int64_t units = int64_t(p.batch) * (p.hkv / p.heads_per_wg) *
+                       (partial ? p.max_partitions - p.part_begin : 1);
+  if (units <= 0) return hipSuccess;
   if (partial)
     hipLaunchKernelGGL((decode_kernel<DT, D, GP, kWaves, pipe_depth<DT, D>(), true>), dim3(unsigned(units)),
                        dim3(kWaves * 64), 0, stream, p);

@@ -22,6 +22,7 @@ struct DecodeParams {
   int32_t batch, hq, hkv, group;
   int32_t num_pages, max_pages, page_shift, capacity;   // capacity = max_pages * page_size
   int32_t partition_tokens, max_partitions;
+  int32_t part_begin;    // split: first partition launched (the ones before are written elsewhere)
   int32_t heads_per_wg;  // KV heads per workgroup (divides hkv and the wave count)
   int32_t tok_stride;    // bytes between consecutive slots of a page (Hkv * D * elem)
   int64_t page_stride;   // bytes per page (page_size * tok_stride)
@@ -56,6 +57,25 @@ struct MergeParams {
   int32_t batch, hq, partition_tokens, max_partitions, capacity;
 };
 
+// Shared-prefix partitions: every sequence's tokens [0, prefix_tokens) sit in the pages
+// prefix_pages[0 .. prefix_tokens / page_size).  Partitions [0, prefix_tokens / partition_tokens)
+// of the split-KV partials are written (bf16 and fp16 only).
+struct PrefixParams {
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* prefix_pages;
+  const int32_t* context_lens;
+  float* partial_out;    // [B, Hq, max_partitions, D]
+  float* partial_lse;    // [B, Hq, max_partitions]
+  float scale_log2;
+  int32_t batch, hq, hkv, group;
+  int32_t num_pages, page_shift, capacity;
+  int32_t prefix_tokens, partition_tokens, max_partitions;
+  int32_t tok_stride;
+  int64_t page_stride;
+};
+
 struct AppendParams {
   const void* k_new;
   const void* v_new;
@@ -84,6 +104,7 @@ int decode_waves();
 hipError_t launch_step(const StepParams& p, int dtype, int head_dim, int group_pad,
                        hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, int dtype, int head_dim, hipStream_t stream);
+hipError_t launch_prefix(const PrefixParams& p, int dtype, int head_dim, hipStream_t stream);
 hipError_t launch_append(const AppendParams& p, hipStream_t stream);
 hipError_t launch_validate(const ValidateParams& p, hipStream_t stream);
 

@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     for n in names:
         assert hasattr(L.lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True, text=True).stdout
@@ -122,6 +122,25 @@ def test_step_rejections(L):
     assert step(out=FAKE + 0x100000) == -1            # out overlaps k_pool
     assert step(sh=shape(L, batch=5000)) == -2        # batch above the step's limit
     assert step(sh=shape(L, batch=0)) == 0
+
+
+def test_cascade_rejections(L):
+    s = shape(L)
+    def c(pages=FAKE + 0xB00000, P=64, PT=64, maxp=1, out=FAKE + 0x500000, sh=s):
+        return L.lib.pkv_paged_decode_cascade(
+            FAKE, FAKE + 0x100000, FAKE + 0x200000, pages, P, FAKE + 0x300000, FAKE + 0x400000,
+            0.1, PT, FAKE + 0x600000, FAKE + 0x700000, maxp, out, None, ctypes.byref(sh), None)
+    assert c(maxp=0) == -1
+    assert c(PT=32, maxp=2) == -2                 # partition not a multiple of 64
+    assert c(P=32) == -1                          # prefix not a multiple of the partition
+    assert c(P=128) == -1                         # prefix beyond the table's 64 tokens
+    assert c(pages=0) == -1
+    assert c(pages=FAKE + 0xB00002) == -1         # misaligned page ids
+    assert c(out=FAKE + 0x600000) == -1           # out overlaps partial_out
+    assert c(sh=shape(L, dtype=0)) == -2          # f32 has no shared-prefix path
+    assert c(sh=shape(L, page_size=16, max_pages_per_seq=640), PT=16 * 640, maxp=1) == -2  # > 512 page ids
+    assert c(sh=shape(L, batch=0)) == 0
+    assert L.last_error().startswith("pkv_paged_decode_cascade")
 
 
 def test_workspace_bytes(L):
