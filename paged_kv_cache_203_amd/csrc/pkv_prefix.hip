@@ -5,9 +5,10 @@
 // rows of all sequences that read one KV head (sequence b, query head kvh * G + g: B x G rows)
 // attend to the same prefix tokens.  Over the prefix, decode attention for those rows is then one
 // dense product per KV head, S = Q K^T (rows x tokens) and O = softmax(S) V, instead of B
-// separate matrix-vector products over the same pages.  A workgroup takes 128 query rows (4 waves
-// x 32 rows) and one partition of the prefix, and streams the partition in blocks of 64 tokens,
-// so each prefix page is read once per 128 rows:
+// separate matrix-vector products over the same pages.  A workgroup takes 128 query rows (8 waves
+// x 16 rows: two waves per SIMD, which measured faster than 4 x 32 at one wave per SIMD) and one
+// partition of the prefix, and streams the partition in blocks of 64 tokens, so each prefix page
+// is read once per 128 rows:
 //  * K block: direct-to-LDS loads, row-major; the 16-byte slices of token t are XOR-swizzled by
 //    t, which keeps the MFMA operand reads free of bank conflicts.
 //  * V block: loaded into registers and written to LDS transposed (dims x tokens, two tokens per
@@ -19,7 +20,8 @@
 //    straight from the S^T registers (tokens 4 kq + i of two adjacent tiles) and V^T is read in
 //    the same token order.  P is split as hi + lo in the 16-bit input type and both halves are
 //    multiplied, which keeps each probability to about 2^-14 relative (bf16) or 2^-20 (fp16).
-// Loads of block n + 1 are in flight while block n is computed (two LDS buffers).  Each (row,
+// Loads of block n + 1 are in flight while block n is computed (two LDS buffers); the rows'
+// lengths, the partition's page ids and the q operands load together at the start.  Each (row,
 // partition) writes its normalised partial output and log-sum-exp in the split-KV layout; the
 // suffix partitions and the merge are the split path's kernels.  Each output element is its own
 // MFMA dot product and the softmax is per row, so a row's bits do not depend on the other rows.
@@ -34,32 +36,34 @@ namespace {
 
 using namespace dev;
 
-constexpr int kPW = 4;                  // waves per workgroup
-constexpr int kRowsWG = kPW * 32;       // query rows per workgroup (two 16-row blocks per wave)
 constexpr int kTB = 64;                 // tokens per block
 
-template <int D>
+// NW waves per workgroup, each with RBW blocks of 16 query rows.
+template <int D, int NW, int RBW>
 struct PrefixGeo {
+  static constexpr int ROWS = NW * 16 * RBW;        // query rows per workgroup
   static constexpr int RB = D * 2;                  // bytes of one token row (16-bit types)
   static constexpr int SPR = RB / 16;               // 16-byte slices per row: 8 or 16
   static constexpr int SWZ = SPR - 1;
   static constexpr int NKL = SPR / 4;               // MFMA k-steps over the head dim: 2 or 4
   static constexpr int KB = kTB * RB;               // K block bytes
-  static constexpr int KDMA = KB / 1024 / kPW;      // direct-to-LDS loads per wave per block
+  static constexpr int KDMA = KB / 1024 / NW;       // direct-to-LDS loads per wave per block
   static constexpr int VST = kTB * 2 + 16;          // bytes per transposed V row (padded)
   static constexpr int VTB = D * VST;               // transposed V block bytes
   static constexpr int NDT = D / 16;                // 16-dim output tiles
-  static constexpr int VTASK = (kTB / 2) * (D / 8) / (kPW * 64);   // (token pair, slice) per thread
+  static constexpr int VTASKS = (kTB / 2) * (D / 8);              // (token pair, slice) tasks
+  static constexpr int VTASK = (VTASKS + NW * 64 - 1) / (NW * 64);  // ... per thread
+  static_assert(KDMA >= 1 && KB % (1024 * NW) == 0, "whole direct-to-LDS loads per wave");
 };
 
 template <int D>
 struct PrefixShared {
-  using Geo = PrefixGeo<D>;
+  using Geo = PrefixGeo<D, 1, 1>;   // the buffers do not depend on the wave layout
   char k[2][Geo::KB] __attribute__((aligned(16)));
   char vt[2][Geo::VTB] __attribute__((aligned(16)));
   int pid[kMaxPrefixPageIds];   // page ids of the partition's prefix pages
-  int end;                      // largest token limit over the workgroup's rows
-  int bad;                      // index of the first out-of-range page id (kMaxPrefixPageIds: none)
+  int wend[16];                 // per wave: largest token limit of its rows
+  int wbad[16];                 // per wave: first out-of-range page id seen (kMaxPrefixPageIds: none)
 };
 
 template <int DT>
@@ -90,9 +94,11 @@ __device__ inline void split_pair(float x0, float x1, uint32_t& hi, uint32_t& lo
   }
 }
 
-template <int DT, int D>
-__global__ __launch_bounds__(kPW * 64) void prefix_kernel(const PrefixParams p) {
-  using Geo = PrefixGeo<D>;
+template <int DT, int D, int NW, int RBW>
+__global__ __launch_bounds__(NW * 64) void prefix_kernel(const PrefixParams p) {
+  using Geo = PrefixGeo<D, NW, RBW>;
+  static_assert(NW <= 16, "per-wave slots");
+  constexpr int kRowsWG = Geo::ROWS;
   constexpr int NKL = Geo::NKL, NDT = Geo::NDT, RB = Geo::RB, VST = Geo::VST;
   __shared__ PrefixShared<D> sm;
 
@@ -113,14 +119,14 @@ __global__ __launch_bounds__(kPW * 64) void prefix_kernel(const PrefixParams p) 
   const int rows = p.batch * p.group;
   const int ps_mask = (1 << p.page_shift) - 1;
 
-  // This lane's two query rows (blocks rb = 0, 1): r = rt * 128 + wave * 32 + rb * 16 + m16.
+  // This lane's query rows (blocks rb < RBW): r = rt * ROWS + (wave * RBW + rb) * 16 + m16.
   // A row attends to prefix tokens t < lim (its length, capped at the partition end); rows past
   // the batch, padding rows and rows longer than the page table allows have lim = 0.
-  int lim[2];
-  int64_t qrow[2];
+  int lim[RBW];
+  int64_t qrow[RBW];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const int r = rt * kRowsWG + wave * 32 + rb * 16 + m16;
+  for (int rb = 0; rb < RBW; ++rb) {
+    const int r = rt * kRowsWG + (wave * RBW + rb) * 16 + m16;
     lim[rb] = 0;
     qrow[rb] = -1;
     if (r < rows) {
@@ -131,34 +137,35 @@ __global__ __launch_bounds__(kPW * 64) void prefix_kernel(const PrefixParams p) 
     }
   }
 
-  if (tid == 0) {
-    sm.end = 0;
-    sm.bad = kMaxPrefixPageIds;
+  int my_end = lim[0], lane_min = lim[0];
+#pragma unroll
+  for (int rb = 1; rb < RBW; ++rb) {
+    my_end = max(my_end, lim[rb]);
+    lane_min = min(lane_min, lim[rb]);
   }
-  __syncthreads();
-  const int my_end = max(lim[0], lim[1]);
-  if (my_end > t_lo) atomicMax(&sm.end, my_end);
-  __syncthreads();
-  const int wg_end = sm.end;
-  if (wg_end <= t_lo) return;   // no row of this tile reaches the partition (uniform)
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) my_end = max(my_end, __shfl_xor(my_end, off));
+  if (lane == 0) sm.wend[wave] = my_end;
 
-  // Blocks cover [t_lo, t_lo + NB * 64), inside the partition (its length is a multiple of 64),
-  // so their pages are prefix pages; stage the ids of all of them.
-  const int NB = (wg_end - t_lo + kTB - 1) / kTB;
-  const int n_ids = (NB * kTB + ps_mask) >> p.page_shift;
-  for (int i = tid; i < n_ids; i += kPW * 64) {
+  // Stage the ids of all the partition's pages (every one is a prefix page: the partition ends
+  // at or before prefix_tokens), and note the first out-of-range one.  These loads, the lengths
+  // above and the q operands below are in flight together.
+  const int n_ids = p.partition_tokens >> p.page_shift;
+  int first_bad = kMaxPrefixPageIds;
+  for (int i = tid; i < n_ids; i += NW * 64) {
     int pg = p.prefix_pages[(t_lo >> p.page_shift) + i];
-    if (pg < 0 || pg >= p.num_pages) {
-      pg = 0;   // read page 0 instead; rows that reach this page get NaN
-      atomicMin(&sm.bad, i);
-    }
+    const bool bad_id = pg < 0 || pg >= p.num_pages;
+    if (bad_id) pg = 0;   // read page 0 instead; rows that reach this page get NaN
     sm.pid[i] = pg;
+    const uint64_t m = __ballot(bad_id);
+    if (m) first_bad = min(first_bad, i - lane + __builtin_ctzll(m));
   }
+  if (lane == 0) sm.wbad[wave] = first_bad;
 
   // Q^T operands: lane holds row m16 of block rb, 16-byte slices 4c + kq (zero past the batch).
-  u32x4 qop[2][NKL];
+  u32x4 qop[RBW][NKL];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
+  for (int rb = 0; rb < RBW; ++rb)
 #pragma unroll
     for (int c = 0; c < NKL; ++c)
       qop[rb][c] = qrow[rb] >= 0
@@ -166,7 +173,16 @@ __global__ __launch_bounds__(kPW * 64) void prefix_kernel(const PrefixParams p) 
                                                        qrow[rb] * RB + 64 * c + 16 * kq)
                        : u32x4{0u, 0u, 0u, 0u};
   __syncthreads();
-  const int64_t bad_from = t_lo + (int64_t(sm.bad) << p.page_shift);   // first token of a bad page
+  int wg_end = 0, bad_idx = kMaxPrefixPageIds;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    wg_end = max(wg_end, sm.wend[w]);
+    bad_idx = min(bad_idx, sm.wbad[w]);
+  }
+  if (wg_end <= t_lo) return;   // no row of this tile reaches the partition (uniform)
+  // Blocks cover [t_lo, t_lo + NB * 64), inside the partition (its length is a multiple of 64).
+  const int NB = (wg_end - t_lo + kTB - 1) / kTB;
+  const int64_t bad_from = t_lo + (int64_t(bad_idx) << p.page_shift);   // first token of a bad page
 
   // Per-lane load geometry.  K: load i of this wave fills LDS bytes (wave * KDMA + i) * 1024 +
   // 16 lane of the block: token kt[i], holding slice kj[i] (the swizzled position's slice).
@@ -178,11 +194,13 @@ __global__ __launch_bounds__(kPW * 64) void prefix_kernel(const PrefixParams p) 
     kj[i] = ((byte % RB) / 16) ^ (kt[i] & Geo::SWZ);
   }
   // V: task k covers tokens 2 tp, 2 tp + 1 and 16-byte slice c.  Four lanes share a token's 64
-  // contiguous bytes; sixteen token pairs per wave.
+  // contiguous bytes; sixteen token pairs per wave.  Threads past the task count have none.
   int vtp[Geo::VTASK], vc[Geo::VTASK];
+  bool vhas[Geo::VTASK];
 #pragma unroll
   for (int k = 0; k < Geo::VTASK; ++k) {
-    const int f = tid + kPW * 64 * k;
+    const int f = tid + NW * 64 * k;
+    vhas[k] = f < Geo::VTASKS;
     const int hi = f / 64;
     vc[k] = (hi % (D / 32)) * 4 + (f % 4);
     vtp[k] = (hi / (D / 32)) * 16 + (f / 4) % 16;
@@ -198,7 +216,7 @@ __global__ __launch_bounds__(kPW * 64) void prefix_kernel(const PrefixParams p) 
     int64_t voff[Geo::VTASK], koff[Geo::KDMA];
 #pragma unroll
     for (int k = 0; k < Geo::VTASK; ++k) {
-      const int rel = rel0 + 2 * vtp[k];
+      const int rel = vhas[k] ? rel0 + 2 * vtp[k] : rel0;
       voff[k] = int64_t(sm.pid[rel >> p.page_shift]) * p.page_stride +
                 int64_t((t_lo + rel) & ps_mask) * p.tok_stride + 16 * vc[k];
     }
@@ -210,6 +228,7 @@ __global__ __launch_bounds__(kPW * 64) void prefix_kernel(const PrefixParams p) 
     }
 #pragma unroll
     for (int k = 0; k < Geo::VTASK; ++k) {
+      if (!vhas[k]) continue;
       const gptr v = to_gptr(vpool + voff[k]);
       vreg[k][0] = *reinterpret_cast<gptr_u32x4>(v);
       vreg[k][1] = *reinterpret_cast<gptr_u32x4>(v + p.tok_stride);
@@ -228,6 +247,7 @@ __global__ __launch_bounds__(kPW * 64) void prefix_kernel(const PrefixParams p) 
     const int t_abs = t_lo + n * kTB;
 #pragma unroll
     for (int k = 0; k < Geo::VTASK; ++k) {
+      if (!vhas[k]) continue;
       const int t0 = t_abs + 2 * vtp[k];
       const u32x4 a = t0 < wg_end ? vreg[k][0] : u32x4{0u, 0u, 0u, 0u};
       const u32x4 b = t0 + 1 < wg_end ? vreg[k][1] : u32x4{0u, 0u, 0u, 0u};
@@ -242,13 +262,15 @@ __global__ __launch_bounds__(kPW * 64) void prefix_kernel(const PrefixParams p) 
     }
   };
 
-  float m_run[2] = {neg_inf(), neg_inf()}, l_run[2] = {0.f, 0.f};
-  f32x4 o[2][NDT];
+  float m_run[RBW], l_run[RBW];
+  f32x4 o[RBW][NDT];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
+  for (int rb = 0; rb < RBW; ++rb) {
+    m_run[rb] = neg_inf();
+    l_run[rb] = 0.f;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) o[rb][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int lane_min = min(lim[0], lim[1]);
+  }
 
   auto compute = [&](int n, int bf) {
     const uint32_t kb = lds_addr(sm.k[bf]);
@@ -256,7 +278,7 @@ __global__ __launch_bounds__(kPW * 64) void prefix_kernel(const PrefixParams p) 
     const int t0 = t_lo + n * kTB;
 
     // ---- S^T tiles = K . Q^T -----------------------------------------------------------------
-    f32x4 s[2][4];
+    f32x4 s[RBW][4];
 #pragma unroll
     for (int tp = 0; tp < 4; tp += 2) {
       u32x4 kop[2 * NKL];
@@ -270,7 +292,7 @@ __global__ __launch_bounds__(kPW * 64) void prefix_kernel(const PrefixParams p) 
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
+        for (int rb = 0; rb < RBW; ++rb) {
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int c = 0; c < NKL; ++c) acc = mfma32<DT>(kop[j * NKL + c], qop[rb][c], acc);
@@ -280,9 +302,10 @@ __global__ __launch_bounds__(kPW * 64) void prefix_kernel(const PrefixParams p) 
 
     // ---- online softmax (lane: row m16 of block rb, tokens 16 tt + 4 kq + i) -----------------
     const bool need_mask = __ballot(lane_min < t0 + kTB) != 0;
-    float alpha[2];
+    float alpha[RBW];
+    bool rescale = false;
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
+    for (int rb = 0; rb < RBW; ++rb) {
       float mx = neg_inf();
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt)
@@ -308,10 +331,11 @@ __global__ __launch_bounds__(kPW * 64) void prefix_kernel(const PrefixParams p) 
           ls += e;
         }
       l_run[rb] = l_run[rb] * alpha[rb] + ls;
+      rescale = rescale || alpha[rb] != 1.f;
     }
-    if (__ballot(alpha[0] != 1.f || alpha[1] != 1.f) != 0) {
+    if (__ballot(rescale) != 0) {
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
+      for (int rb = 0; rb < RBW; ++rb)
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) o[rb][dt] *= alpha[rb];
     }
@@ -319,9 +343,9 @@ __global__ __launch_bounds__(kPW * 64) void prefix_kernel(const PrefixParams p) 
     // ---- O^T += V^T . P, 32 tokens per MFMA k-step -------------------------------------------
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      u32x4 ph[2], pl[2];
+      u32x4 ph[RBW], pl[RBW];
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
+      for (int rb = 0; rb < RBW; ++rb) {
         uint32_t h[4], l[4];
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
@@ -348,7 +372,7 @@ __global__ __launch_bounds__(kPW * 64) void prefix_kernel(const PrefixParams p) 
       for (int dt = 0; dt < NDT; ++dt) {
         const u32x4 av = {va[dt][0].x, va[dt][0].y, va[dt][1].x, va[dt][1].y};
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
+        for (int rb = 0; rb < RBW; ++rb) {
           o[rb][dt] = mfma32<DT>(av, ph[rb], o[rb][dt]);
           o[rb][dt] = mfma32<DT>(av, pl[rb], o[rb][dt]);
         }
@@ -373,7 +397,7 @@ __global__ __launch_bounds__(kPW * 64) void prefix_kernel(const PrefixParams p) 
 
   // ---- normalised partials (lane: dims 16 dt + 4 kq + i of row m16) ----------------------------
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < RBW; ++rb) {
     const float l = sum_rows4(l_run[rb]);
     if (lim[rb] <= t_lo) continue;   // the row does not reach this partition: not written
     const int64_t orow = qrow[rb] * p.max_partitions + part;
@@ -388,12 +412,18 @@ __global__ __launch_bounds__(kPW * 64) void prefix_kernel(const PrefixParams p) 
   }
 }
 
+// Wave layout: kPrefixWaves waves of kPrefixRowBlocks x 16 query rows.
+constexpr int kPrefixWaves = 8, kPrefixRowBlocks = 1;
+
 template <int DT, int D>
 hipError_t launch_prefix_t(const PrefixParams& p, hipStream_t stream) {
-  const int64_t tiles = (int64_t(p.batch) * p.group + kRowsWG - 1) / kRowsWG;
+  constexpr int NW = kPrefixWaves, RBW = kPrefixRowBlocks;
+  constexpr int ROWS = PrefixGeo<D, NW, RBW>::ROWS;
+  const int64_t tiles = (int64_t(p.batch) * p.group + ROWS - 1) / ROWS;
   const int64_t units = tiles * p.hkv * (p.prefix_tokens / p.partition_tokens);
   if (units == 0) return hipSuccess;
-  hipLaunchKernelGGL((prefix_kernel<DT, D>), dim3(unsigned(units)), dim3(kPW * 64), 0, stream, p);
+  hipLaunchKernelGGL((prefix_kernel<DT, D, NW, RBW>), dim3(unsigned(units)), dim3(NW * 64), 0,
+                     stream, p);
   return hipGetLastError();
 }
 
