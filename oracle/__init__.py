@@ -9,3 +9,4 @@ from .paged_attention import (to_f64, gather_rows, paged_decode_attention,  # no
                               paged_decode_attention_partial, num_partitions, lse_merge,
                               paged_kv_append, validate_metadata, STATUS_PAGE_RANGE,
                               STATUS_CAPACITY, STATUS_APPEND_ALIAS)
+from . import rope  # noqa: F401,E402

@@ -5,4 +5,4 @@ part of the attention arithmetic, so both the HIP library and the CPU oracle can
 """
 from .configs import CONFIGS, DecodeConfig, config, default_scale  # noqa: F401
 from .generate import (Workload, make_workload, relabel_pages, subset_rows,  # noqa: F401
-                       unshare_prefix, fill_normal, draw_lengths)
+                       unshare_prefix, fill_normal, draw_lengths, rope_tables)

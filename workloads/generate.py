@@ -277,3 +277,14 @@ def subset_rows(w: Workload, rows: Sequence[int]) -> Workload:
         append_lens=None if w.append_lens is None else w.append_lens[rows].copy(),
         k_new=None if w.k_new is None else w.k_new[rows].copy(),
         v_new=None if w.v_new is None else w.v_new[rows].copy())
+
+
+def rope_tables(positions: int, head_dim: int, base: float = 10000.0):
+    """A rotary cache as a model holds it: float32 ``cos``, ``sin`` of shape
+    ``[positions, head_dim / 2]`` with angle ``p * base ** (-2 i / head_dim)`` for row p, pair i,
+    evaluated in float64 and rounded once to float32.  It is an input of the rotary step (the
+    step applies it); nothing here rotates anything."""
+    i = np.arange(head_dim // 2, dtype=np.float64)
+    inv = base ** (-2.0 * i / head_dim)
+    ang = np.arange(positions, dtype=np.float64)[:, None] * inv[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
