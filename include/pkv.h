@@ -170,6 +170,29 @@ int pkv_paged_kv_append(const void* k_new, const void* v_new, void* k_pool, void
                         const int32_t* page_table, const int32_t* context_lens,
                         const pkv_shape* shape, void* stream);
 
+/* Fused rotary embedding + paged KV append for the decode step's new token.
+ *
+ * For every row with L = context_lens[b] >= 0 (the new token's position), in one launch:
+ *   q_out[b, h, :] = RoPE(q[b, h, :], L) for every query head h;
+ *   the K pool slot L % PS of page page_table[b][L / PS] = RoPE(k_new[b], L), bit for bit;
+ *   the same slot of the V pool = v_new[b], bit for bit.
+ * RoPE is the rotate-half form: pair i < D/2 of a head is (x[i], x[i + D/2]), turned to
+ * (x[i] c - x[i + D/2] s, x[i + D/2] c + x[i] s) with c = rope_cos[L][i], s = rope_sin[L][i]
+ * (the caller's rotary cache, float32 [rope_positions, D/2], 16-byte aligned), computed in
+ * float32 with each product and sum rounded to nearest even, then rounded to the element type.
+ * The pages name this step (CacheIR page, "Compiler Example": rope(q, k) ahead of the decode
+ * attention, fused_rmsnorm_qkv_rope ahead of paged_attention_decode; TorchInferno page,
+ * "OpenAI-Compatible Serving": a decode rotary-append kernel) but not its formula; the
+ * rotate-half form is that of the Llama/Mistral/Qwen decoders they target.
+ * Padding rows (L < 0) copy q to q_out and write nothing.  Rows with L >= rope_positions or
+ * L >= max_pages_per_seq * page_size get NaN in q_out and write nothing; a row whose page id is
+ * out of range writes nothing.  q_out must not overlap any input.  Attention afterwards uses
+ * q_out and context_lens + 1. */
+int pkv_rope_kv_append(const void* q, const void* k_new, const void* v_new, void* k_pool,
+                       void* v_pool, const int32_t* page_table, const int32_t* context_lens,
+                       const float* rope_cos, const float* rope_sin, int32_t rope_positions,
+                       void* q_out, const pkv_shape* shape, void* stream);
+
 /* One whole decode step in one call, with the work split evenly over the GPU.
  *
  * With k_new and v_new non-NULL, every sequence's new K and V rows are first written into the

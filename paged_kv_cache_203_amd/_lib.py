@@ -57,6 +57,8 @@ _SIGNATURES = {
     "pkv_paged_decode_cascade": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _vp, _vp, ctypes.c_float,
                                                 _i32, _vp, _vp, _i32, _vp, _vp,
                                                 ctypes.POINTER(PkvShape), _vp]),
+    "pkv_rope_kv_append": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp,
+                                          ctypes.POINTER(PkvShape), _vp]),
     "pkv_decode_step_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(PkvShape)]),
     "pkv_partial_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(PkvShape), _i32]),
     "pkv_last_error": (ctypes.c_char_p, []),
@@ -351,6 +353,31 @@ def paged_kv_append(k_new, v_new, k_pool, v_pool, page_table, context_lens) -> N
     _check(lib.pkv_paged_kv_append(k_new.data_ptr(), v_new.data_ptr(), k_pool.data_ptr(),
                                    v_pool.data_ptr(), page_table.data_ptr(),
                                    context_lens.data_ptr(), ctypes.byref(s), _stream(dev)))
+
+
+def rope_kv_append(q, k_new, v_new, k_pool, v_pool, page_table, context_lens, rope_cos, rope_sin,
+                   q_out=None):
+    """Rotary embedding + append of the new token at position ``context_lens[b]``: q rotated into
+    ``q_out`` (returned), k_new rotated and v_new written into the pools.  ``rope_cos`` /
+    ``rope_sin`` are the float32 rotary cache ``[positions, D/2]``."""
+    torch = _torch()
+    s = _attention_shape(q, k_pool, v_pool, page_table, context_lens)
+    for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+        _require(t, n, dtype=q.dtype, ndim=3, device=q.device)
+        if tuple(t.shape) != (s.batch, s.num_kv_heads, s.head_dim):
+            raise ValueError(f"{n} must be [B, Hkv, D]")
+    for t, n in ((rope_cos, "rope_cos"), (rope_sin, "rope_sin")):
+        _require(t, n, dtype=torch.float32, ndim=2, device=q.device)
+        if t.shape[1] != s.head_dim // 2 or t.shape != rope_cos.shape:
+            raise ValueError(f"{n} must be [positions, D/2]")
+    if q_out is None:
+        q_out = torch.empty_like(q)
+    _require(q_out, "q_out", dtype=q.dtype, ndim=3, device=q.device)
+    _check(lib.pkv_rope_kv_append(
+        q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+        page_table.data_ptr(), context_lens.data_ptr(), rope_cos.data_ptr(), rope_sin.data_ptr(),
+        int(rope_cos.shape[0]), q_out.data_ptr(), ctypes.byref(s), _stream(q.device)))
+    return q_out
 
 
 def validate_metadata(page_table, context_lens, num_pages: int, page_size: int,

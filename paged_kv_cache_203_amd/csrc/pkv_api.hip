@@ -291,6 +291,42 @@ int pkv_paged_kv_append(const void* k_new, const void* v_new, void* k_pool, void
                        "pkv_paged_kv_append");
 }
 
+int pkv_rope_kv_append(const void* q, const void* k_new, const void* v_new, void* k_pool,
+                       void* v_pool, const int32_t* page_table, const int32_t* context_lens,
+                       const float* rope_cos, const float* rope_sin, int32_t rope_positions,
+                       void* q_out, const pkv_shape* shape, void* stream) {
+  std::string msg;
+  const int rc = pkv::check_rope_append(q, k_new, v_new, k_pool, v_pool, page_table, context_lens,
+                                        rope_cos, rope_sin, rope_positions, q_out, shape, msg);
+  if (rc) return set_error(rc, "pkv_rope_kv_append: " + msg);
+  if (shape->batch == 0) return PKV_OK;
+  pkv::RopeParams p{};
+  p.a.k_new = k_new;
+  p.a.v_new = v_new;
+  p.a.k_pool = k_pool;
+  p.a.v_pool = v_pool;
+  p.a.page_table = page_table;
+  p.a.context_lens = context_lens;
+  p.a.batch = shape->batch;
+  p.a.num_pages = shape->num_pages;
+  p.a.max_pages = shape->max_pages_per_seq;
+  p.a.page_shift = log2_exact(shape->page_size);
+  p.a.capacity = shape->max_pages_per_seq * shape->page_size;
+  p.a.row_bytes = shape->num_kv_heads * shape->head_dim * pkv::elem_bytes(shape->dtype);
+  p.a.page_stride = int64_t(shape->page_size) * p.a.row_bytes;
+  p.q = q;
+  p.q_out = q_out;
+  p.rope_cos = rope_cos;
+  p.rope_sin = rope_sin;
+  p.rope_rows = rope_positions;
+  p.hq = shape->num_q_heads;
+  p.hkv = shape->num_kv_heads;
+  (void)hipGetLastError();
+  return launch_status(pkv::launch_rope_append(p, shape->dtype, shape->head_dim,
+                                               static_cast<hipStream_t>(stream)),
+                       "pkv_rope_kv_append");
+}
+
 int pkv_validate_metadata(const int32_t* page_table, const int32_t* context_lens,
                           int32_t extra_tokens, int32_t check_append_unique,
                           int32_t* device_status, const pkv_shape* shape, void* stream) {

@@ -310,6 +310,31 @@ int check_step(const void* q, const void* k_new, const void* v_new, const void* 
   return PKV_OK;
 }
 
+int check_rope_append(const void* q, const void* k_new, const void* v_new, const void* k_pool,
+                      const void* v_pool, const int32_t* page_table, const int32_t* context_lens,
+                      const float* rope_cos, const float* rope_sin, int32_t rope_positions,
+                      const void* q_out, const pkv_shape* s, std::string& msg) {
+  int rc = check_append(k_new, v_new, k_pool, v_pool, page_table, context_lens, s, msg);
+  if (rc) return rc;
+  if (rope_positions <= 0) return fail(msg, PKV_EINVAL, "rope_positions must be > 0");
+  if (s->batch == 0) return PKV_OK;
+  if (!q || !q_out || !rope_cos || !rope_sin)
+    return fail(msg, PKV_EINVAL, "q, q_out, rope_cos and rope_sin must be non-NULL");
+  if (!aligned(q, 16) || !aligned(q_out, 16) || !aligned(rope_cos, 16) || !aligned(rope_sin, 16))
+    return fail(msg, PKV_EUNSUPPORTED, "q, q_out, rope_cos and rope_sin must be 16-byte aligned");
+  const Extents x = extents(*s);
+  const uint64_t tab = uint64_t(rope_positions) * (s->head_dim / 2) * 4;
+  const void* ins[9] = {q, k_new, v_new, k_pool, v_pool, page_table, context_lens, rope_cos, rope_sin};
+  const uint64_t ins_n[9] = {x.q, x.new_rows, x.new_rows, x.pool, x.pool, x.table, x.lens, tab, tab};
+  for (int i = 0; i < 9; ++i)
+    if (overlaps(q_out, x.q, ins[i], ins_n[i])) return fail(msg, PKV_EINVAL, "q_out overlaps another buffer");
+  for (int i = 3; i < 5; ++i)
+    for (int j : {0, 7, 8})
+      if (overlaps(ins[i], ins_n[i], ins[j], ins_n[j]))
+        return fail(msg, PKV_EINVAL, "a pool overlaps q or the rotary cache");
+  return PKV_OK;
+}
+
 int check_validate(const int32_t* page_table, const int32_t* context_lens, int32_t extra_tokens,
                    const int32_t* device_status, const pkv_shape* s, std::string& msg) {
   int rc = check_shape(s, msg);

@@ -46,6 +46,11 @@ int check_append(const void* k_new, const void* v_new, const void* k_pool, const
                  const int32_t* page_table, const int32_t* context_lens, const pkv_shape* s,
                  std::string& msg);
 
+int check_rope_append(const void* q, const void* k_new, const void* v_new, const void* k_pool,
+                      const void* v_pool, const int32_t* page_table, const int32_t* context_lens,
+                      const float* rope_cos, const float* rope_sin, int32_t rope_positions,
+                      const void* q_out, const pkv_shape* s, std::string& msg);
+
 // Largest batch the balanced decode step supports (its tile prefix lives in LDS), and most query
 // heads (keeps a sequence's piece partials within 32-bit buffer offsets).
 constexpr int kMaxStepBatch = 4096;

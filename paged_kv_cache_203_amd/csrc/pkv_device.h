@@ -105,6 +105,43 @@ __device__ inline void store_row(void* base, int64_t idx, const float (&x)[N]) {
   }
 }
 
+// Rotary embedding of one pair (x1, x2) = (x[i], x[i + D/2]) by the angle whose cosine and sine
+// are c and s: y1 = x1 c - x2 s, y2 = x2 c + x1 s, in float32 with each product and each sum
+// rounded to nearest even (contraction into fused multiply-adds is switched off here, so the
+// result is the same on every path that calls it).
+__device__ inline void rope_pair(float x1, float x2, float c, float s, float& y1, float& y2) {
+#pragma clang fp contract(off)
+  const float a = x1 * c, b = x2 * s, e = x2 * c, f = x1 * s;
+  y1 = a - b;
+  y2 = e + f;
+}
+
+// 16 bytes of elements <-> floats: 8 for 16-bit types, 4 for float32.
+template <int DT>
+struct Vec16 {
+  static constexpr int N = DT == DT_F32 ? 4 : 8;
+  __device__ static void unpack(const u32x4& w, float (&x)[N]) {
+    if constexpr (DT == DT_F32) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = __uint_as_float(w[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) unpack2<DT>(w[i], x[2 * i], x[2 * i + 1]);
+    }
+  }
+  __device__ static u32x4 pack(const float (&x)[N]) {
+    u32x4 w;
+    if constexpr (DT == DT_F32) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = __float_as_uint(x[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = elem_bits<DT>(x[2 * i]) | (elem_bits<DT>(x[2 * i + 1]) << 16);
+    }
+    return w;
+  }
+};
+
 // Global-address-space byte pointer (loads through it are global_load, never flat_load).
 typedef const __attribute__((address_space(1))) char* gptr;
 typedef const __attribute__((address_space(1))) u32x4* gptr_u32x4;

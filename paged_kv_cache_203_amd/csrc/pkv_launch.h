@@ -88,6 +88,18 @@ struct AppendParams {
   int64_t page_stride;
 };
 
+// Fused rotary embedding + append: q -> q_out rotated, k_new rotated into the K pool, v_new into
+// the V pool, at position context_lens[b]; the rotary cache is rope_cos / rope_sin
+// [rope_rows, D/2] float32.
+struct RopeParams {
+  AppendParams a;
+  const void* q;
+  void* q_out;
+  const float* rope_cos;
+  const float* rope_sin;
+  int32_t rope_rows, hq, hkv;
+};
+
 struct ValidateParams {
   const int32_t* page_table;
   const int32_t* context_lens;
@@ -106,6 +118,7 @@ hipError_t launch_step(const StepParams& p, int dtype, int head_dim, int group_p
 hipError_t launch_merge(const MergeParams& p, int dtype, int head_dim, hipStream_t stream);
 hipError_t launch_prefix(const PrefixParams& p, int dtype, int head_dim, hipStream_t stream);
 hipError_t launch_append(const AppendParams& p, hipStream_t stream);
+hipError_t launch_rope_append(const RopeParams& p, int dtype, int head_dim, hipStream_t stream);
 hipError_t launch_validate(const ValidateParams& p, hipStream_t stream);
 
 }  // namespace pkv

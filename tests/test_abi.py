@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(L.lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True, text=True).stdout
@@ -141,6 +141,22 @@ def test_cascade_rejections(L):
     assert c(sh=shape(L, page_size=16, max_pages_per_seq=640), PT=16 * 640, maxp=1) == -2  # > 512 page ids
     assert c(sh=shape(L, batch=0)) == 0
     assert L.last_error().startswith("pkv_paged_decode_cascade")
+
+
+def test_rope_append_rejections(L):
+    s = shape(L)
+    def r(q=FAKE, qo=FAKE + 0x800000, cos=FAKE + 0xC00000, sin=FAKE + 0xD00000, rows=64, kn=FAKE + 0xA00000):
+        return L.lib.pkv_rope_kv_append(q, kn, FAKE + 0xA10000, FAKE + 0x100000, FAKE + 0x200000,
+                                        FAKE + 0x300000, FAKE + 0x400000, cos, sin, rows, qo,
+                                        ctypes.byref(s), None)
+    assert r(rows=0) == -1
+    assert r(cos=0) == -1
+    assert r(qo=0) == -1
+    assert r(cos=FAKE + 0xC00004) == -2          # rotary cache not 16-byte aligned
+    assert r(qo=FAKE) == -1                      # q_out overlaps q
+    assert r(qo=FAKE + 0xC00000) == -1           # q_out overlaps the rotary cache
+    assert r(kn=0) == -1
+    assert L.last_error().startswith("pkv_rope_kv_append")
 
 
 def test_workspace_bytes(L):
