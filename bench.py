@@ -49,6 +49,9 @@ def parse():
     ap.add_argument("--path", choices=["step", "split", "single", "cascade"], default="step",
                     help="cascade: shared-prefix decode (prefix-shared workloads only)")
     ap.add_argument("--partition-tokens", type=int, default=None)
+    ap.add_argument("--rope", action="store_true",
+                    help="step path: rotate the new key and the query in the same launch "
+                         "(rotary cache with base 500000)")
     ap.add_argument("--replicas", type=int, default=None,
                     help="pool replicas rotated per step (default: enough for >= 2 GB)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -250,6 +253,12 @@ def main():
     prefix_tokens = w.shared_pages * PS
     prefix_pages = torch.from_numpy(np.ascontiguousarray(
         w.page_table[int(np.argmax(w.context_lens > 0)), :w.shared_pages])).to(dev)
+    rope = {}
+    if args.rope:
+        if args.path != "step":
+            raise SystemExit("--rope applies to the step path")
+        rc, rs = W.rope_tables(w.page_table.shape[1] * PS + 1, D, 500000.0)
+        rope = dict(rope_cos=torch.from_numpy(rc).to(dev), rope_sin=torch.from_numpy(rs).to(dev))
     ws = None
     if args.path == "step":
         ws = torch.zeros(pkv.decode_step_workspace_bytes(q, k0, table), dtype=torch.uint8, device=dev)
@@ -260,7 +269,7 @@ def main():
             if ev is not None:
                 ev[0].record(stream)
             pkv.paged_decode_step(q, kp, vp, table, alens, scale, k_new=kn, v_new=vn, out=out,
-                                  workspace=ws)
+                                  workspace=ws, **rope)
             if ev is not None:
                 ev[1].record(stream)
             return
@@ -338,6 +347,7 @@ def main():
             "batch": B, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D, "page_size": PS,
             "context_lens": list(cfg.lengths), "seed": w.seed, "live_tokens": w.logical_tokens(),
             "partition_tokens": P if args.path in ("split", "cascade") else None, "path": args.path,
+            "rope": bool(args.rope),
             "pool_replicas": R,
             "step_bytes": nb["step"], "kv_bytes": nb["kv"],
         },

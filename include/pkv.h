@@ -224,6 +224,20 @@ int pkv_paged_decode_step(const void* q, const void* k_new, const void* v_new, v
                           float scale, void* workspace, size_t workspace_bytes, void* out,
                           float* lse_out, const pkv_shape* shape, void* stream);
 
+/* The decode step with the rotary embedding fused in: as pkv_paged_decode_step with an append,
+ * except that the new key is written rotated, and the query rotated, both at position
+ * context_lens[b], exactly as pkv_rope_kv_append computes them (same float32 steps, same
+ * rounding); attention then covers context_lens[b] + 1 tokens.  One launch does the rotation,
+ * the append and the attention.  rope_cos, rope_sin, k_new and v_new must be non-NULL.  A row
+ * whose position has no row in the rotary cache (context_lens[b] >= rope_positions) writes a NaN
+ * key, so its output is NaN. */
+int pkv_paged_decode_step_rope(const void* q, const void* k_new, const void* v_new, void* k_pool,
+                               void* v_pool, const int32_t* page_table,
+                               const int32_t* context_lens, const float* rope_cos,
+                               const float* rope_sin, int32_t rope_positions, float scale,
+                               void* workspace, size_t workspace_bytes, void* out, float* lse_out,
+                               const pkv_shape* shape, void* stream);
+
 /* Workspace bytes pkv_paged_decode_step needs on the current device (0 on a bad shape or when
  * no device is available). */
 size_t pkv_decode_step_workspace_bytes(const pkv_shape* shape);

@@ -59,6 +59,9 @@ _SIGNATURES = {
                                                 ctypes.POINTER(PkvShape), _vp]),
     "pkv_rope_kv_append": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp,
                                           ctypes.POINTER(PkvShape), _vp]),
+    "pkv_paged_decode_step_rope": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
+                                                  ctypes.c_float, _vp, ctypes.c_size_t, _vp, _vp,
+                                                  ctypes.POINTER(PkvShape), _vp]),
     "pkv_decode_step_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(PkvShape)]),
     "pkv_partial_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(PkvShape), _i32]),
     "pkv_last_error": (ctypes.c_char_p, []),
@@ -301,9 +304,12 @@ def decode_step_workspace_bytes(q, k_pool, page_table) -> int:
 
 
 def paged_decode_step(q, k_pool, v_pool, page_table, context_lens, scale: Optional[float] = None,
-                      k_new=None, v_new=None, out=None, lse_out=None, workspace=None):
+                      k_new=None, v_new=None, out=None, lse_out=None, workspace=None,
+                      rope_cos=None, rope_sin=None):
     """Balanced decode step: optional append of k_new/v_new at context_lens[b], then attention
-    over context_lens[b] (+1 with the append).  Returns ``out [B, Hq, D]``."""
+    over context_lens[b] (+1 with the append).  With ``rope_cos`` / ``rope_sin`` (the float32
+    rotary cache ``[positions, D/2]``; needs the append) the new key and the query are rotated
+    at position context_lens[b] in the same launch.  Returns ``out [B, Hq, D]``."""
     torch = _torch()
     s = _attention_shape(q, k_pool, v_pool, page_table, context_lens)
     if (k_new is None) != (v_new is None):
@@ -325,6 +331,20 @@ def paged_decode_step(q, k_pool, v_pool, page_table, context_lens, scale: Option
         workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=q.device)
     _require(workspace, "workspace", dtype=torch.uint8, ndim=1, device=q.device)
     scale = _default_scale(s.head_dim) if scale is None else float(scale)
+    if rope_cos is not None or rope_sin is not None:
+        if rope_cos is None or rope_sin is None or k_new is None:
+            raise ValueError("the rotary step needs rope_cos, rope_sin and the appended rows")
+        for t, n in ((rope_cos, "rope_cos"), (rope_sin, "rope_sin")):
+            _require(t, n, dtype=torch.float32, ndim=2, device=q.device)
+            if t.shape[1] != s.head_dim // 2 or t.shape != rope_cos.shape:
+                raise ValueError(f"{n} must be [positions, D/2]")
+        _check(lib.pkv_paged_decode_step_rope(
+            q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_pool.data_ptr(),
+            v_pool.data_ptr(), page_table.data_ptr(), context_lens.data_ptr(),
+            rope_cos.data_ptr(), rope_sin.data_ptr(), int(rope_cos.shape[0]), scale,
+            workspace.data_ptr(), workspace.numel(), out.data_ptr(), lse_ptr, ctypes.byref(s),
+            _stream(q.device)))
+        return out
     _check(lib.pkv_paged_decode_step(
         q.data_ptr(), None if k_new is None else k_new.data_ptr(),
         None if v_new is None else v_new.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),

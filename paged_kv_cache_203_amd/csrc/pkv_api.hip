@@ -205,19 +205,24 @@ size_t pkv_decode_step_workspace_bytes(const pkv_shape* shape) {
   return size_t(pkv::step_workspace(*shape, groups, heads_per_workgroup(shape->num_kv_heads)).bytes);
 }
 
-int pkv_paged_decode_step(const void* q, const void* k_new, const void* v_new, void* k_pool,
-                          void* v_pool, const int32_t* page_table, const int32_t* context_lens,
-                          float scale, void* workspace, size_t workspace_bytes, void* out,
-                          float* lse_out, const pkv_shape* shape, void* stream) {
+namespace {
+int decode_step(const char* name, const void* q, const void* k_new, const void* v_new,
+                void* k_pool, void* v_pool, const int32_t* page_table,
+                const int32_t* context_lens, const float* rope_cos, const float* rope_sin,
+                int32_t rope_positions, float scale, void* workspace, size_t workspace_bytes,
+                void* out, float* lse_out, const pkv_shape* shape, void* stream) {
   std::string msg;
   int rc = pkv::check_shape(shape, msg);
-  if (rc) return set_error(rc, "pkv_paged_decode_step: " + msg);
+  if (rc) return set_error(rc, std::string(name) + ": " + msg);
   const int64_t groups = shape->batch ? step_groups(*shape) : 1;
   const pkv::StepWorkspace ws =
       pkv::step_workspace(*shape, groups ? groups : 1, heads_per_workgroup(shape->num_kv_heads));
   rc = pkv::check_step(q, k_new, v_new, k_pool, v_pool, page_table, context_lens, scale, workspace,
                        workspace_bytes, groups ? ws.bytes : 0, out, lse_out, shape, msg);
-  if (rc) return set_error(rc, "pkv_paged_decode_step: " + msg);
+  if (!rc && rope_cos)
+    rc = pkv::check_rope_tables(k_new, rope_cos, rope_sin, rope_positions, out, lse_out, workspace,
+                                workspace_bytes, shape, msg);
+  if (rc) return set_error(rc, std::string(name) + ": " + msg);
   if (shape->batch == 0) return PKV_OK;
   pkv::StepParams p{};
   p.a = decode_params(q, k_pool, v_pool, page_table, context_lens, scale, *shape);
@@ -234,10 +239,37 @@ int pkv_paged_decode_step(const void* q, const void* k_new, const void* v_new, v
   p.lse_out = lse_out;
   p.groups = int32_t(groups);
   p.append = k_new ? 1 : 0;
+  p.rope_cos = rope_cos;
+  p.rope_sin = rope_sin;
+  p.rope_rows = rope_positions;
   (void)hipGetLastError();
   return launch_status(pkv::launch_step(p, shape->dtype, shape->head_dim, group_pad(p.a.group),
                                         static_cast<hipStream_t>(stream)),
-                       "pkv_paged_decode_step");
+                       name);
+}
+}  // namespace
+
+int pkv_paged_decode_step(const void* q, const void* k_new, const void* v_new, void* k_pool,
+                          void* v_pool, const int32_t* page_table, const int32_t* context_lens,
+                          float scale, void* workspace, size_t workspace_bytes, void* out,
+                          float* lse_out, const pkv_shape* shape, void* stream) {
+  return decode_step("pkv_paged_decode_step", q, k_new, v_new, k_pool, v_pool, page_table,
+                     context_lens, nullptr, nullptr, 0, scale, workspace, workspace_bytes, out,
+                     lse_out, shape, stream);
+}
+
+int pkv_paged_decode_step_rope(const void* q, const void* k_new, const void* v_new, void* k_pool,
+                               void* v_pool, const int32_t* page_table,
+                               const int32_t* context_lens, const float* rope_cos,
+                               const float* rope_sin, int32_t rope_positions, float scale,
+                               void* workspace, size_t workspace_bytes, void* out, float* lse_out,
+                               const pkv_shape* shape, void* stream) {
+  if (!rope_cos || !rope_sin || !k_new || !v_new)
+    return set_error(PKV_EINVAL, "pkv_paged_decode_step_rope: rope_cos, rope_sin, k_new and "
+                                 "v_new must be non-NULL (the rotated key is appended)");
+  return decode_step("pkv_paged_decode_step_rope", q, k_new, v_new, k_pool, v_pool, page_table,
+                     context_lens, rope_cos, rope_sin, rope_positions, scale, workspace,
+                     workspace_bytes, out, lse_out, shape, stream);
 }
 
 int pkv_lse_merge(const float* partial_out, const float* partial_lse,

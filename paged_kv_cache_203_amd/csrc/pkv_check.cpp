@@ -310,6 +310,25 @@ int check_step(const void* q, const void* k_new, const void* v_new, const void* 
   return PKV_OK;
 }
 
+int check_rope_tables(const void* k_new, const float* rope_cos, const float* rope_sin,
+                      int32_t rope_positions, const void* out, const float* lse_out,
+                      const void* workspace, size_t workspace_bytes, const pkv_shape* s,
+                      std::string& msg) {
+  if (!k_new) return fail(msg, PKV_EINVAL, "the rotary embedding needs the appended rows");
+  if (rope_positions <= 0) return fail(msg, PKV_EINVAL, "rope_positions must be > 0");
+  if (!rope_cos || !rope_sin) return fail(msg, PKV_EINVAL, "rope_cos and rope_sin must be non-NULL");
+  if (!aligned(rope_cos, 16) || !aligned(rope_sin, 16))
+    return fail(msg, PKV_EUNSUPPORTED, "rope_cos and rope_sin must be 16-byte aligned");
+  const Extents x = extents(*s);
+  const uint64_t tab = uint64_t(rope_positions) * (s->head_dim / 2) * 4;
+  const uint64_t lo = uint64_t(s->batch) * s->num_q_heads * 4;
+  for (const void* t : {static_cast<const void*>(rope_cos), static_cast<const void*>(rope_sin)})
+    if (overlaps(t, tab, out, x.out) || (lse_out && overlaps(t, tab, lse_out, lo)) ||
+        overlaps(t, tab, workspace, workspace_bytes))
+      return fail(msg, PKV_EINVAL, "the rotary cache overlaps an output or the workspace");
+  return PKV_OK;
+}
+
 int check_rope_append(const void* q, const void* k_new, const void* v_new, const void* k_pool,
                       const void* v_pool, const int32_t* page_table, const int32_t* context_lens,
                       const float* rope_cos, const float* rope_sin, int32_t rope_positions,

@@ -46,6 +46,13 @@ int check_append(const void* k_new, const void* v_new, const void* k_pool, const
                  const int32_t* page_table, const int32_t* context_lens, const pkv_shape* s,
                  std::string& msg);
 
+// The rotary cache of the fused step: non-NULL, 16-byte aligned, rope_positions > 0, and no
+// overlap with the step's outputs or workspace.
+int check_rope_tables(const void* k_new, const float* rope_cos, const float* rope_sin,
+                      int32_t rope_positions, const void* out, const float* lse_out,
+                      const void* workspace, size_t workspace_bytes, const pkv_shape* s,
+                      std::string& msg);
+
 int check_rope_append(const void* q, const void* k_new, const void* v_new, const void* k_pool,
                       const void* v_pool, const int32_t* page_table, const int32_t* context_lens,
                       const float* rope_cos, const float* rope_sin, int32_t rope_positions,

@@ -88,12 +88,20 @@ struct HeadSource {
   int t_begin, t_end;        // t_begin is a multiple of 16
   int sub, stride;           // this wave takes tiles sub, sub + stride, ...
   const char* q_group;       // q rows of the wave's GQA group (used by HeadPipe::prefetch)
+  // Rotary embedding of q (HeadPipe with ROPE): the cache rows [D/2] at the query's position;
+  // rope_pos < 0 leaves q as it is.
+  const float* rope_cos;
+  const float* rope_sin;
+  int rope_pos;
 };
 
-template <int DT, int D, int GP, int DEPTH>
+template <int DT, int D, int GP, int DEPTH, bool ROPE = false>
 struct HeadPipe {
   using Geo = TileGeo<DT, D>;
   static constexpr int NKL = Geo::NKL, VPL = Geo::VPL, VW = Geo::VW;
+  // Rotary embedding: slice 4c + kq of q (elements (4c + kq) * RW4 * 4 ...) pairs with slice
+  // 4(c + NKL/2) + kq, half a head further on, in the same lane.
+  static constexpr int RW4 = Vec16<DT>::N / 4;   // float4s of cos (or sin) per slice
   static constexpr uint32_t VSTAGE0 = DEPTH * Geo::KTILE;   // LDS offset of V stage 0
 
   // per-lane constants
@@ -111,6 +119,7 @@ struct HeadPipe {
   u32x4 q_pref[NKL];
   int pv_pref;
   bool pref_ready = false;
+  f32x4 rope_cs[ROPE ? NKL / 2 : 1][2][RW4];   // prefetched cos, sin of this lane's pairs
   float m_run, l_run, o[GP][VPL];
   bool bad;
 
@@ -165,7 +174,35 @@ struct HeadPipe {
                             : u32x4{0u, 0u, 0u, 0u};
     const int n_my = tiles_of(s);
     pv_pref = n_my > 0 ? chunk_pages(s, 0, min(kChunk, n_my)) : 0;
+    if constexpr (ROPE) {
+      const bool on = s.rope_pos >= 0;
+      const int64_t row = int64_t(on ? s.rope_pos : 0) * (D / 2);
+#pragma unroll
+      for (int c = 0; c < NKL / 2; ++c)
+#pragma unroll
+        for (int r = 0; r < RW4; ++r) {
+          const int64_t i = row + (4 * c + kq) * Vec16<DT>::N + 4 * r;
+          rope_cs[c][0][r] = on ? *reinterpret_cast<const f32x4*>(s.rope_cos + i) : f32x4{1.f, 1.f, 1.f, 1.f};
+          rope_cs[c][1][r] = on ? *reinterpret_cast<const f32x4*>(s.rope_sin + i) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
     pref_ready = true;
+  }
+
+  // Rotate the q operand by the prefetched cache rows (each pair's halves are in this lane).
+  __device__ void rope_q() {
+    constexpr int N = Vec16<DT>::N;
+#pragma unroll
+    for (int c = 0; c < NKL / 2; ++c) {
+      float x1[N], x2[N], y1[N], y2[N];
+      Vec16<DT>::unpack(qreg[c], x1);
+      Vec16<DT>::unpack(qreg[c + NKL / 2], x2);
+#pragma unroll
+      for (int j = 0; j < N; ++j)
+        rope_pair(x1[j], x2[j], rope_cs[c][0][j / 4][j % 4], rope_cs[c][1][j / 4][j % 4], y1[j], y2[j]);
+      qreg[c] = Vec16<DT>::pack(y1);
+      qreg[c + NKL / 2] = Vec16<DT>::pack(y2);
+    }
   }
 
   __device__ void reset() {
@@ -345,6 +382,7 @@ struct HeadPipe {
     if (pref_ready) {
 #pragma unroll
       for (int c = 0; c < NKL; ++c) qreg[c] = q_pref[c];
+      if constexpr (ROPE) rope_q();
       pref_ready = false;
     }
     for (int c0 = 0; c0 < n_my; c0 += kChunk) {
@@ -726,7 +764,7 @@ __device__ void step_merge(const StepParams& p, const StepSplit& sp, int b, int 
   __syncthreads();   // `flags` may be rewritten next
 }
 
-template <int DT, int D, int GP, int NW, int DEPTH>
+template <int DT, int D, int GP, int NW, int DEPTH, bool ROPE>
 __global__ __launch_bounds__(NW * 64) void step_kernel(const StepParams p) {
   using Geo = TileGeo<DT, D>;
   using Shm = DecodeShared<DT, D, GP, NW, DEPTH>;
@@ -770,7 +808,7 @@ __global__ __launch_bounds__(NW * 64) void step_kernel(const StepParams p) {
 
   int b = sp.seq_of_tile(lo);   // the sequence holding tile `lo`
 
-  HeadPipe<DT, D, GP, DEPTH> hp;
+  HeadPipe<DT, D, GP, DEPTH, ROPE> hp;
   hp.init(a.tok_stride, lds_addr(sm.w[wave]), &sm.p[wave][0][0], &sm.a[wave][0]);
 
   // The appended rows of every sequence whose last tile lies in this range are written first;
@@ -788,10 +826,38 @@ __global__ __launch_bounds__(NW * 64) void step_kernel(const StepParams p) {
                           int64_t(hg) * HPW * Geo::RB;
       const int64_t srco = int64_t(bb) * row_bytes + int64_t(hg) * HPW * Geo::RB;
       for (int i = threadIdx.x; i < HPW * Geo::RB / 16; i += NW * 64) {
-        const u32x4 kv = *reinterpret_cast<const u32x4*>(static_cast<const char*>(p.k_new) + srco + 16 * i);
         const u32x4 vv = *reinterpret_cast<const u32x4*>(static_cast<const char*>(p.v_new) + srco + 16 * i);
-        *reinterpret_cast<u32x4*>(static_cast<char*>(p.k_pool_w) + dst + 16 * i) = kv;
         *reinterpret_cast<u32x4*>(static_cast<char*>(p.v_pool_w) + dst + 16 * i) = vv;
+        if constexpr (!ROPE) {
+          const u32x4 kv = *reinterpret_cast<const u32x4*>(static_cast<const char*>(p.k_new) + srco + 16 * i);
+          *reinterpret_cast<u32x4*>(static_cast<char*>(p.k_pool_w) + dst + 16 * i) = kv;
+        }
+      }
+      if constexpr (ROPE) {
+        // The key is written rotated: thread i takes 16-byte chunk j of the first half of a head
+        // and the matching chunk of the second half (the pairs' partners).  A position without
+        // a row in the rotary cache writes NaN, so the row's output shows it.
+        using V = Vec16<DT>;
+        constexpr int HALF = Geo::RB / 32;   // 16-byte chunks per half head
+        const bool on = L < p.rope_rows;
+        const float* cs = p.rope_cos + int64_t(on ? L : 0) * (D / 2);
+        const float* sn = p.rope_sin + int64_t(on ? L : 0) * (D / 2);
+        for (int i = threadIdx.x; i < HPW * HALF; i += NW * 64) {
+          const int j = i % HALF;
+          const int64_t off = int64_t(i / HALF) * Geo::RB + 16 * j;
+          const char* src = static_cast<const char*>(p.k_new) + srco + off;
+          float x1[V::N], x2[V::N], y1[V::N], y2[V::N];
+          V::unpack(*reinterpret_cast<const u32x4*>(src), x1);
+          V::unpack(*reinterpret_cast<const u32x4*>(src + Geo::RB / 2), x2);
+#pragma unroll
+          for (int e = 0; e < V::N; ++e) {
+            rope_pair(x1[e], x2[e], cs[j * V::N + e], sn[j * V::N + e], y1[e], y2[e]);
+            if (!on) y1[e] = y2[e] = qnan();
+          }
+          char* d = static_cast<char*>(p.k_pool_w) + dst + off;
+          *reinterpret_cast<u32x4*>(d) = V::pack(y1);
+          *reinterpret_cast<u32x4*>(d + Geo::RB / 2) = V::pack(y2);
+        }
       }
     }
     __syncthreads();
@@ -815,6 +881,13 @@ __global__ __launch_bounds__(NW * 64) void step_kernel(const StepParams p) {
     src.sub = wave / HPW;
     src.stride = WPH;
     src.q_group = static_cast<const char*>(a.q) + (int64_t(bb) * a.hq + int64_t(kvh) * G) * Geo::RB;
+    src.rope_cos = p.rope_cos;
+    src.rope_sin = p.rope_sin;
+    src.rope_pos = -1;
+    if constexpr (ROPE) {
+      const int L = a.context_lens[bb];   // the new token's position
+      src.rope_pos = L >= 0 && L < p.rope_rows ? L : -1;
+    }
     return src;
   };
   // The next sequence after bb with tiles in this range, or B.
@@ -1034,7 +1107,12 @@ hipError_t launch_decode_t(const DecodeParams& p, bool partial, hipStream_t stre
 template <int DT, int D, int GP>
 hipError_t launch_step_t(const StepParams& p, hipStream_t stream) {
   const int nhg = p.a.hkv / p.a.heads_per_wg;
-  hipLaunchKernelGGL((step_kernel<DT, D, GP, kWaves, pipe_depth<DT, D>()>), dim3(unsigned(p.groups * nhg)),
+  if (p.rope_cos) {
+    hipLaunchKernelGGL((step_kernel<DT, D, GP, kWaves, pipe_depth<DT, D>(), true>), dim3(unsigned(p.groups * nhg)),
+                       dim3(kWaves * 64), 0, stream, p);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((step_kernel<DT, D, GP, kWaves, pipe_depth<DT, D>(), false>), dim3(unsigned(p.groups * nhg)),
                      dim3(kWaves * 64), 0, stream, p);
   return hipGetLastError();
 }

@@ -46,6 +46,11 @@ struct StepParams {
   float* lse_out;        // may be null
   int32_t groups;        // token-range groups per head group
   int32_t append;        // 1: append k_new/v_new at context_lens[b], attend over +1
+  // Rotary embedding (with the append only): the new key is written rotated and q is rotated
+  // in registers, both at position context_lens[b]; rope_cos / rope_sin [rope_rows, D/2].
+  const float* rope_cos; // null: no rotation
+  const float* rope_sin;
+  int32_t rope_rows;
 };
 
 struct MergeParams {

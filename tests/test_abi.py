@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(L.lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True, text=True).stdout
@@ -157,6 +157,17 @@ def test_rope_append_rejections(L):
     assert r(qo=FAKE + 0xC00000) == -1           # q_out overlaps the rotary cache
     assert r(kn=0) == -1
     assert L.last_error().startswith("pkv_rope_kv_append")
+
+
+def test_step_rope_rejections(L):
+    s = shape(L)
+    def st(cos=FAKE + 0xC00000, sin=FAKE + 0xD00000, rows=64, kn=FAKE + 0xA00000, vn=FAKE + 0xA10000):
+        return L.lib.pkv_paged_decode_step_rope(
+            FAKE, kn, vn, FAKE + 0x100000, FAKE + 0x200000, FAKE + 0x300000, FAKE + 0x400000,
+            cos, sin, rows, 0.1, FAKE + 0x900000, 1 << 30, FAKE + 0x500000, None, ctypes.byref(s), None)
+    assert st(cos=0) == -1
+    assert st(kn=0, vn=0) == -1                   # the rotated key must be appended
+    assert L.last_error().startswith("pkv_paged_decode_step_rope")
 
 
 def test_workspace_bytes(L):

@@ -112,3 +112,46 @@ def test_rope_append_rows_without_a_cache_row_get_nan_and_write_nothing(pkv):
                                           np.where(keep, lens, -1), cos, sin, w.dtype)
     assert same_bits(d.k_pool, kp, w.dtype) and same_bits(d.v_pool, vp, w.dtype)
     assert same_bits(q_out[torch.from_numpy(keep)], q_rot[keep], w.dtype)
+
+
+STEP_CASES = [
+    ("llama3-8b-bf16-b64", dict(batch=9, lengths=("uniform", 1, 700)), 500000.0),
+    ("qwen2-7b-gqa7-bf16-append", dict(batch=7, lengths=("loguniform", 1, 900)), 1000000.0),
+    ("prefix-shared-fp16-b128", dict(batch=6, lengths=("prefix", 64, 1, 90)), 10000.0),
+    ("tiny-fp32", None, 10000.0),
+]
+
+
+@pytest.mark.parametrize("name,scaled,base", STEP_CASES)
+def test_step_with_rope_is_rope_append_then_step(pkv, name, scaled, base):
+    """One launch (rotation, append, attention) against the oracle, and bitwise against the two
+    launches it replaces: pkv_rope_kv_append, then the step without an append."""
+    cfg = W.config(name)
+    if scaled:
+        cfg = cfg.scaled(**scaled)
+    w = W.make_workload(cfg, pad_rows=[2] if cfg.batch > 3 else ())
+    log(f"case step+rope {cfg.name}")
+    kn, vn, alens = appended(w)
+    P = int(w.page_table.shape[1] * w.cfg.page_size)
+    cos, sin = W.rope_tables(P, w.q.shape[2], base)
+    cos_t, sin_t = torch.from_numpy(cos).cuda(), torch.from_numpy(sin).cuda()
+    d = DeviceWorkload(w)
+    alens_t = torch.from_numpy(alens).cuda()
+    out = pkv.paged_decode_step(d.q, d.k_pool, d.v_pool, d.page_table, alens_t, d.scale,
+                                k_new=to_device(kn, w.dtype), v_new=to_device(vn, w.dtype),
+                                rope_cos=cos_t, rope_sin=sin_t)
+    torch.cuda.synchronize()
+    q_rot, kp, vp = O.rope.rope_kv_append(w.q, w.k_pool, w.v_pool, kn, vn, w.page_table, alens,
+                                          cos, sin, w.dtype)
+    assert same_bits(d.k_pool, kp, w.dtype) and same_bits(d.v_pool, vp, w.dtype)
+    lens = np.where(alens >= 0, alens + 1, 0).astype(np.int32)
+    ref, _ = O.paged_decode_attention(q_rot, kp, vp, w.page_table, lens, w.scale, w.dtype)
+    assert_parity(to_f64(out), ref, w.dtype, f"step+rope {cfg.name}")
+    # the same step as two launches
+    d2 = DeviceWorkload(w)
+    q2 = pkv.rope_kv_append(d2.q, to_device(kn, w.dtype), to_device(vn, w.dtype), d2.k_pool,
+                            d2.v_pool, d2.page_table, alens_t, cos_t, sin_t)
+    out2 = pkv.paged_decode_step(q2, d2.k_pool, d2.v_pool, d2.page_table,
+                                 torch.from_numpy(lens).cuda(), d2.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.uint8), out2.view(torch.uint8))
