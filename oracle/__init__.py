@@ -6,6 +6,7 @@ share no code: the oracle is a plain, slow restatement of the definitions, writt
 float64, so that a reader can check it against the pages by eye.
 """
 from .paged_attention import (to_f64, gather_rows, paged_decode_attention,  # noqa: F401
+                              paged_multi_query_attention,
                               paged_decode_attention_partial, num_partitions, lse_merge,
                               paged_kv_append, validate_metadata, STATUS_PAGE_RANGE,
                               STATUS_CAPACITY, STATUS_APPEND_ALIAS)

@@ -29,6 +29,9 @@ What is computed, and where the pages state it:
 Precision: inputs are decoded exactly to float64 (bf16 from raw bits), arithmetic is float64, the
 softmax scale is the float32 value the caller passes, widened exactly.
 
+Multi-query decode (T new tokens per sequence, causal) is the decode of each query over its own
+prefix of the sequence.
+
 Parity pins live in tests/test_oracle.py: a loop-only brute force over contiguous K/V, closed forms
 (one token, two tokens, constant V, zero query, identical keys), invariance under page relabelling
 and prefix unsharing, GQA equal to MHA over repeated KV heads, and the LSE-merge identity.
@@ -128,6 +131,26 @@ def paged_decode_attention(q, k_pool, v_pool, page_table, context_lens, scale, d
             for g in range(G):
                 h = kvh * G + g
                 out[b, h], lse[b, h] = _softmax_attend(sc * (K @ qf[b, h]), V)
+    return out, lse
+
+
+def paged_multi_query_attention(q, k_pool, v_pool, page_table, context_lens, scale, dtype):
+    """Causal attention of T new query tokens per sequence, ``q [B, T, Hq, D]``.
+
+    ``context_lens[b]`` counts every token of the sequence, the T new ones included (their K/V
+    rows are already in the pages).  Query ``j`` sits at position ``L - T + j`` and attends to
+    tokens ``[0, L - T + j]``: it is the decode of one query over ``L - T + 1 + j`` tokens.
+    Returns ``(out [B, T, Hq, D], lse [B, T, Hq])``; a query with no tokens gets 0 / -inf.
+    (Infinity docs, "Short shared prefix qualification": a tile of up to 32 query rows of
+    suffix tokens after a cached context; the causal rule is that of decoder self-attention.)"""
+    B, T, Hq, D = q.shape
+    lens = np.asarray(context_lens, dtype=np.int64)
+    out = np.zeros((B, T, Hq, D), dtype=np.float64)
+    lse = np.full((B, T, Hq), -np.inf, dtype=np.float64)
+    for j in range(T):
+        Lj = np.where(lens > 0, np.maximum(lens - T + 1 + j, 0), 0)
+        out[:, j], lse[:, j] = paged_decode_attention(np.ascontiguousarray(q[:, j]), k_pool,
+                                                      v_pool, page_table, Lj, scale, dtype)
     return out, lse
 
 

@@ -448,3 +448,68 @@ def test_golden_hand_derived_example():
     np.testing.assert_allclose(out, np.array(g["expected_out"]), rtol=0, atol=1e-15)
     want_lse = [[a + math.log(n) for a, n in row] for row in g["expected_lse"]]
     np.testing.assert_allclose(lse, np.array(want_lse), rtol=0, atol=1e-15)
+
+
+# ----------------------------------------------------------------------------------------------
+# multi-query (causal) decode
+# ----------------------------------------------------------------------------------------------
+
+def brute_causal(qs, K_log, V_log, scale):
+    """Loop-only causal attention of T queries qs [T][Hq][D] that are the last T tokens of the
+    sequence K_log/V_log [L][Hkv][D]: query j sees rows 0 .. L - T + j (an explicit mask)."""
+    T, L = len(qs), len(K_log)
+    outs = []
+    for j in range(T):
+        last = L - T + j
+        outs.append(brute_decode(qs[j], K_log[:last + 1], V_log[:last + 1], scale)[0])
+    return outs
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_multi_query_matches_causal_brute_force(seed):
+    rng = np.random.default_rng(seed)
+    B, T, Hkv, G, D, PS = 3, 4, 2, 2, 8, 4
+    lens = [5, 9, 4]
+    rows_k = [rng.standard_normal((L, Hkv, D)) for L in lens]
+    rows_v = [rng.standard_normal((L, Hkv, D)) for L in lens]
+    pk, table = scatter_to_pool(rows_k, PS, 12, np.random.default_rng(seed + 7))
+    pv = np.full_like(pk, np.nan)
+    for b in range(B):
+        for i, page in enumerate(table[b]):
+            if page >= 0:
+                chunk = rows_v[b][i * PS:(i + 1) * PS]
+                pv[page, :len(chunk)] = chunk
+    q = rng.standard_normal((B, T, Hkv * G, D)).astype(np.float32)
+    out, lse = O.paged_multi_query_attention(q, pk.astype(np.float32), pv.astype(np.float32),
+                                             table, np.array(lens), 0.3, "f32")
+    for b in range(B):
+        ref = brute_causal(q[b].astype(np.float64).tolist(),
+                           rows_k[b].astype(np.float32).astype(np.float64).tolist(),
+                           rows_v[b].astype(np.float32).astype(np.float64).tolist(),
+                           float(np.float32(0.3)))
+        assert np.abs(out[b] - np.array(ref)).max() < 1e-12
+
+
+def test_multi_query_is_causal_and_last_query_is_the_decode():
+    rng = np.random.default_rng(3)
+    B, T, Hkv, G, D, PS = 2, 3, 1, 4, 16, 4
+    lens = np.array([10, 7])
+    rows_k = [rng.standard_normal((L, Hkv, D)) for L in lens]
+    rows_v = [rng.standard_normal((L, Hkv, D)) for L in lens]
+    pk, table = scatter_to_pool(rows_k, PS, 8, np.random.default_rng(1))
+    pv, _ = scatter_to_pool(rows_v, PS, 8, np.random.default_rng(1))
+    q = rng.standard_normal((B, T, G, D))
+    out, _ = O.paged_multi_query_attention(q, pk, pv, table, lens, 0.25, "f32")
+    full, _ = O.paged_decode_attention(np.ascontiguousarray(q[:, -1]), pk, pv, table, lens, 0.25, "f32")
+    assert np.abs(out[:, -1] - full).max() < 1e-13
+    # changing the last token's key moves only the last query of that sequence
+    pk2 = pk.copy()
+    b, L = 0, int(lens[0])
+    pk2[table[b, (L - 1) // PS], (L - 1) % PS] += 3.0
+    out2, _ = O.paged_multi_query_attention(q, pk2, pv, table, lens, 0.25, "f32")
+    assert np.array_equal(out2[0, :-1], out[0, :-1]) and np.array_equal(out2[1], out[1])
+    assert np.abs(out2[0, -1] - out[0, -1]).max() > 1e-6
+    # a sequence shorter than T: its first queries see nothing
+    out3, lse3 = O.paged_multi_query_attention(q, pk, pv, table, np.array([2, 7]), 0.25, "f32")
+    assert np.all(out3[0, 0] == 0) and np.all(np.isneginf(lse3[0, 0]))
+    assert np.isfinite(lse3[0, 1:]).all()
