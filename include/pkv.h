@@ -170,6 +170,35 @@ int pkv_paged_kv_append(const void* k_new, const void* v_new, void* k_pool, void
                         const int32_t* page_table, const int32_t* context_lens,
                         const pkv_shape* shape, void* stream);
 
+/* Multi-query paged decode: T = num_query_tokens new tokens per sequence (speculative or
+ * suffix decode), attending causally.
+ *
+ * q and out are [batch, T, num_q_heads, head_dim].  context_lens[b] = L_b counts every token of
+ * the sequence, the T new ones included (their K/V rows are already in the pages).  Query j
+ * (0-based) sits at position L_b - T + j and attends to tokens 0 .. L_b - T + j through
+ * page_table as usual, so each query is the decode of one token over its own prefix; queries
+ * with no tokens (L_b - T + 1 + j <= 0) and padding rows get out = 0, lse = -inf.
+ * Two launches on `stream`: for every (sequence, KV head, partition of P = partition_tokens
+ * tokens), the G x T query rows attend to the partition's tokens as one dense product on the
+ * matrix cores (the K and V of the partition are read once for all T queries; the same kernel
+ * as the shared-prefix path's prefix partitions), writing partials to partial_out / partial_lse
+ * ([batch, T, num_q_heads, max_partitions, (head_dim)], float32); then the log-sum-exp merge of
+ * each query's ceil((L_b - T + 1 + j) / P) partitions into out and lse_out ([batch, T,
+ * num_q_heads], float32, may be NULL).  The pages tile decode attention over up to 32 query rows
+ * of suffix tokens after a cached context (Infinity docs, "Short shared prefix qualification");
+ * the causal rule is that of decoder self-attention.
+ *
+ * Requirements: dtype bf16 or f16 (else PKV_EUNSUPPORTED); partition_tokens a multiple of 64 and
+ * of page_size with partition_tokens / page_size <= 512; max_partitions >=
+ * ceil(max_pages_per_seq * page_size / partition_tokens).  A row's bits depend only on its own
+ * sequence, its query index and P. */
+int pkv_paged_decode_multi_query(const void* q, const void* k_pool, const void* v_pool,
+                                 const int32_t* page_table, const int32_t* context_lens,
+                                 int32_t num_query_tokens, float scale, int32_t partition_tokens,
+                                 float* partial_out, float* partial_lse, int32_t max_partitions,
+                                 void* out, float* lse_out, const pkv_shape* shape,
+                                 void* stream);
+
 /* Fused rotary embedding + paged KV append for the decode step's new token.
  *
  * For every row with L = context_lens[b] >= 0 (the new token's position), in one launch:

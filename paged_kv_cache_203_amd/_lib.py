@@ -62,6 +62,9 @@ _SIGNATURES = {
     "pkv_paged_decode_step_rope": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
                                                   ctypes.c_float, _vp, ctypes.c_size_t, _vp, _vp,
                                                   ctypes.POINTER(PkvShape), _vp]),
+    "pkv_paged_decode_multi_query": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, ctypes.c_float,
+                                                    _i32, _vp, _vp, _i32, _vp, _vp,
+                                                    ctypes.POINTER(PkvShape), _vp]),
     "pkv_decode_step_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(PkvShape)]),
     "pkv_partial_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(PkvShape), _i32]),
     "pkv_last_error": (ctypes.c_char_p, []),
@@ -293,6 +296,45 @@ def paged_decode_cascade(q, k_pool, v_pool, prefix_pages, prefix_tokens: int, pa
         int(prefix_tokens), page_table.data_ptr(), context_lens.data_ptr(), scale,
         int(partition_tokens), partial_out.data_ptr(), partial_lse.data_ptr(),
         int(max_partitions), out.data_ptr(), lse_ptr, ctypes.byref(s), _stream(q.device)))
+    return out
+
+
+def paged_decode_multi_query(q, k_pool, v_pool, page_table, context_lens, partition_tokens: int = 256,
+                             scale: Optional[float] = None, out=None, lse_out=None,
+                             partial_out=None, partial_lse=None):
+    """Causal decode of T new tokens per sequence: ``q [B, T, Hq, D]``; ``context_lens[b]``
+    counts the T new tokens too.  Returns ``out [B, T, Hq, D]``."""
+    torch = _torch()
+    _require(q, "q", ndim=4)
+    B, T, Hq, D = q.shape
+    s = _attention_shape(torch.empty((B, Hq, D), dtype=q.dtype, device=q.device), k_pool,
+                         v_pool, page_table, context_lens)   # shapes only
+    maxp = (partial_lse.shape[3] if partial_lse is not None else
+            partitions_needed(s.page_size, s.max_pages_per_seq, partition_tokens))
+    if partial_out is None:
+        partial_out = torch.empty((B, T, Hq, maxp, D), dtype=torch.float32, device=q.device)
+    if partial_lse is None:
+        partial_lse = torch.empty((B, T, Hq, maxp), dtype=torch.float32, device=q.device)
+    _require(partial_out, "partial_out", dtype=torch.float32, ndim=5, device=q.device)
+    _require(partial_lse, "partial_lse", dtype=torch.float32, ndim=4, device=q.device)
+    if (tuple(partial_out.shape) != (B, T, Hq, maxp, D)
+            or tuple(partial_lse.shape) != (B, T, Hq, maxp)):
+        raise ValueError("partial buffers have the wrong shape")
+    if out is None:
+        out = torch.empty_like(q)
+    _require(out, "out", dtype=q.dtype, ndim=4, device=q.device)
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must be [B, T, Hq, D]")
+    lse_ptr = None
+    if lse_out is not None:
+        _require(lse_out, "lse_out", dtype=torch.float32, ndim=3, device=q.device)
+        lse_ptr = lse_out.data_ptr()
+    scale = _default_scale(s.head_dim) if scale is None else float(scale)
+    _check(lib.pkv_paged_decode_multi_query(
+        q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), page_table.data_ptr(),
+        context_lens.data_ptr(), int(T), scale, int(partition_tokens), partial_out.data_ptr(),
+        partial_lse.data_ptr(), int(maxp), out.data_ptr(), lse_ptr, ctypes.byref(s),
+        _stream(q.device)))
     return out
 
 

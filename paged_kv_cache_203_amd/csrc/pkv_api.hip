@@ -197,6 +197,65 @@ int pkv_paged_decode_cascade(const void* q, const void* k_pool, const void* v_po
                        "pkv_paged_decode_cascade (merge)");
 }
 
+int pkv_paged_decode_multi_query(const void* q, const void* k_pool, const void* v_pool,
+                                 const int32_t* page_table, const int32_t* context_lens,
+                                 int32_t num_query_tokens, float scale, int32_t partition_tokens,
+                                 float* partial_out, float* partial_lse, int32_t max_partitions,
+                                 void* out, float* lse_out, const pkv_shape* shape,
+                                 void* stream) {
+  std::string msg;
+  const int rc = pkv::check_multi_query(q, k_pool, v_pool, page_table, context_lens,
+                                        num_query_tokens, scale, partition_tokens, partial_out,
+                                        partial_lse, max_partitions, out, lse_out, shape, msg);
+  if (rc) return set_error(rc, "pkv_paged_decode_multi_query: " + msg);
+  if (shape->batch == 0) return PKV_OK;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const pkv::DecodeParams d = decode_params(q, k_pool, v_pool, page_table, context_lens, scale, *shape);
+  (void)hipGetLastError();
+  // 1. Every (sequence, KV head, partition): its G x T query rows against the partition's
+  //    tokens on the matrix cores, query j masked past its own position.
+  pkv::PrefixParams pp{};
+  pp.q = q;
+  pp.k_pool = k_pool;
+  pp.v_pool = v_pool;
+  pp.context_lens = context_lens;
+  pp.partial_out = partial_out;
+  pp.partial_lse = partial_lse;
+  pp.scale_log2 = d.scale_log2;
+  pp.batch = d.batch;
+  pp.hq = d.hq;
+  pp.hkv = d.hkv;
+  pp.group = d.group;
+  pp.num_pages = d.num_pages;
+  pp.page_shift = d.page_shift;
+  pp.capacity = d.capacity;
+  pp.partition_tokens = partition_tokens;
+  pp.max_partitions = max_partitions;
+  pp.tok_stride = d.tok_stride;
+  pp.page_stride = d.page_stride;
+  pp.page_table = page_table;
+  pp.max_pages = d.max_pages;
+  pp.q_tokens = num_query_tokens;
+  int r = launch_status(pkv::launch_prefix(pp, shape->dtype, shape->head_dim, st),
+                        "pkv_paged_decode_multi_query (partitions)");
+  if (r) return r;
+  // 2. The merge of each (sequence, query token)'s partitions.
+  pkv::MergeParams m{};
+  m.partial_out = partial_out;
+  m.partial_lse = partial_lse;
+  m.context_lens = context_lens;
+  m.out = out;
+  m.lse_out = lse_out;
+  m.batch = shape->batch;
+  m.hq = shape->num_q_heads;
+  m.partition_tokens = partition_tokens;
+  m.max_partitions = max_partitions;
+  m.capacity = d.capacity;
+  m.q_tokens = num_query_tokens;
+  return launch_status(pkv::launch_merge(m, shape->dtype, shape->head_dim, st),
+                       "pkv_paged_decode_multi_query (merge)");
+}
+
 size_t pkv_decode_step_workspace_bytes(const pkv_shape* shape) {
   std::string msg;
   if (pkv::check_shape(shape, msg) != PKV_OK) return 0;

@@ -220,6 +220,57 @@ int check_cascade(const void* q, const void* k_pool, const void* v_pool,
   return PKV_OK;
 }
 
+int check_multi_query(const void* q, const void* k_pool, const void* v_pool,
+                      const int32_t* page_table, const int32_t* context_lens, int32_t q_tokens,
+                      float scale, int32_t partition_tokens, const float* partial_out,
+                      const float* partial_lse, int32_t max_partitions, const void* out,
+                      const float* lse_out, const pkv_shape* s, std::string& msg) {
+  int rc = check_shape(s, msg);
+  if (rc) return rc;
+  if (q_tokens < 1) return fail(msg, PKV_EINVAL, "num_query_tokens must be >= 1");
+  if (int64_t(s->batch) * q_tokens * s->num_q_heads > INT32_MAX / 2)
+    return fail(msg, PKV_EINVAL, "batch * num_query_tokens * num_q_heads too large");
+  if (s->dtype != PKV_BF16 && s->dtype != PKV_F16)
+    return fail(msg, PKV_EUNSUPPORTED, "multi-query decode supports bf16 and f16 only");
+  if (partition_tokens <= 0 || partition_tokens % s->page_size != 0 ||
+      partition_tokens % kPrefixBlock != 0)
+    return fail(msg, PKV_EUNSUPPORTED, "partition_tokens must be a positive multiple of 64 and of page_size");
+  if (partition_tokens / s->page_size > kMaxPrefixPageIds)
+    return fail(msg, PKV_EUNSUPPORTED, "partition_tokens / page_size must be <= 512");
+  if (max_partitions <= 0) return fail(msg, PKV_EINVAL, "max_partitions must be > 0");
+  if (max_partitions < partitions_needed(*s, partition_tokens))
+    return fail(msg, PKV_EWORKSPACE,
+                "max_partitions < ceil(max_pages_per_seq * page_size / partition_tokens)");
+  if (s->batch == 0) return PKV_OK;
+  rc = check_attention_inputs(q, k_pool, v_pool, page_table, context_lens, scale, msg);
+  if (rc) return rc;
+  if (!partial_out || !partial_lse || !out)
+    return fail(msg, PKV_EINVAL, "partial_out, partial_lse and out must be non-NULL");
+  if (!aligned(partial_out, 16) || !aligned(out, 16))
+    return fail(msg, PKV_EUNSUPPORTED, "partial_out and out must be 16-byte aligned");
+  if (!aligned(partial_lse, 4) || (lse_out && !aligned(lse_out, 4)))
+    return fail(msg, PKV_EINVAL, "partial_lse and lse_out must be 4-byte aligned");
+  const Extents x = extents(*s);
+  const uint64_t rows = uint64_t(s->batch) * q_tokens * s->num_q_heads;
+  const uint64_t qn = rows * s->head_dim * elem_bytes(s->dtype);
+  const uint64_t po = rows * uint64_t(max_partitions) * s->head_dim * 4;
+  const uint64_t pl = rows * uint64_t(max_partitions) * 4;
+  const uint64_t lo = rows * 4;
+  const void* ins[5] = {q, k_pool, v_pool, page_table, context_lens};
+  const uint64_t ins_n[5] = {qn, x.pool, x.pool, x.table, x.lens};
+  const void* outs[4] = {partial_out, partial_lse, out, lse_out};
+  const uint64_t outs_n[4] = {po, pl, qn, lse_out ? lo : 0};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 5; ++j)
+      if (overlaps(outs[i], outs_n[i], ins[j], ins_n[j]))
+        return fail(msg, PKV_EINVAL, "an output or the partials overlap an input");
+    for (int j = 0; j < i; ++j)
+      if (overlaps(outs[i], outs_n[i], outs[j], outs_n[j]))
+        return fail(msg, PKV_EINVAL, "partials, out and lse_out must not overlap");
+  }
+  return PKV_OK;
+}
+
 int check_append(const void* k_new, const void* v_new, const void* k_pool, const void* v_pool,
                  const int32_t* page_table, const int32_t* context_lens, const pkv_shape* s,
                  std::string& msg) {

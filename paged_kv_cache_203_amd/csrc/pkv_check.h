@@ -74,6 +74,12 @@ int check_cascade(const void* q, const void* k_pool, const void* v_pool,
                   const float* partial_out, const float* partial_lse, int32_t max_partitions,
                   const void* out, const float* lse_out, const pkv_shape* s, std::string& msg);
 
+int check_multi_query(const void* q, const void* k_pool, const void* v_pool,
+                      const int32_t* page_table, const int32_t* context_lens, int32_t q_tokens,
+                      float scale, int32_t partition_tokens, const float* partial_out,
+                      const float* partial_lse, int32_t max_partitions, const void* out,
+                      const float* lse_out, const pkv_shape* s, std::string& msg);
+
 // Workspace layout of the balanced decode step for `groups` workgroup ranges (all offsets
 // 256-byte aligned).  The arrival counters (one per sequence and group of heads_per_wg KV heads)
 // come first and are sized for kMaxStepBatch sequences, so their place does not move with the

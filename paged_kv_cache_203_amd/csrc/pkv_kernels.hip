@@ -997,9 +997,10 @@ template <int DT, int D>
 __global__ __launch_bounds__(64) void merge_kernel(const MergeParams p) {
   constexpr int DPL = D / 64;   // dims per lane
   const int lane = threadIdx.x;
-  const int b = blockIdx.x / p.hq;
+  const int b = blockIdx.x / p.hq;   // row (sequence, or sequence x query token)
   const int h = blockIdx.x % p.hq;
-  const int L = p.context_lens[b];
+  int L = p.context_lens[p.q_tokens > 1 ? b / p.q_tokens : b];
+  if (p.q_tokens > 1 && L > 0 && L <= p.capacity) L = max(L - p.q_tokens + 1 + b % p.q_tokens, 0);
   const int64_t orow = (int64_t(b) * p.hq + h) * D;
   if (L <= 0 || L > p.capacity) {
     const float fill = L <= 0 ? 0.f : qnan();
@@ -1157,7 +1158,7 @@ struct StepLaunch {
 
 template <int DT>
 hipError_t launch_merge_dt(const MergeParams& p, int head_dim, hipStream_t stream) {
-  const int64_t units = int64_t(p.batch) * p.hq;
+  const int64_t units = int64_t(p.batch) * (p.q_tokens > 1 ? p.q_tokens : 1) * p.hq;
   if (units == 0) return hipSuccess;
   if (head_dim == 64)
     hipLaunchKernelGGL((merge_kernel<DT, 64>), dim3(unsigned(units)), dim3(64), 0, stream, p);

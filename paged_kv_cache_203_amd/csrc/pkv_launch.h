@@ -60,6 +60,9 @@ struct MergeParams {
   void* out;
   float* lse_out;        // may be null
   int32_t batch, hq, partition_tokens, max_partitions, capacity;
+  // q_tokens = T > 1: rows are (sequence, query token j) pairs, batch * T of them, and row
+  // (b, j) covers L_b - T + 1 + j tokens (multi-query decode); 0 or 1: one query per sequence.
+  int32_t q_tokens;
 };
 
 // Shared-prefix partitions: every sequence's tokens [0, prefix_tokens) sit in the pages
@@ -79,6 +82,10 @@ struct PrefixParams {
   int32_t prefix_tokens, partition_tokens, max_partitions;
   int32_t tok_stride;
   int64_t page_stride;
+  // Multi-query decode (q_tokens = T > 0): q [B, T, Hq, D], partials [B, T, Hq, max_partitions, D];
+  // every sequence's pages come from its page_table row (max_pages entries); prefix_* unused.
+  const int32_t* page_table;
+  int32_t max_pages, q_tokens;
 };
 
 struct AppendParams {

@@ -94,7 +94,11 @@ __device__ inline void split_pair(float x0, float x1, uint32_t& hi, uint32_t& lo
   }
 }
 
-template <int DT, int D, int NW, int RBW>
+// MQ = false: the shared-prefix partitions (rows: every sequence's query heads of one KV head;
+// pages: prefix_pages).  MQ = true: multi-query decode (rows: the T new query tokens x G heads of
+// one sequence and KV head, query j limited to tokens t <= L - T + j; pages: the sequence's own
+// page-table row).
+template <int DT, int D, int NW, int RBW, bool MQ>
 __global__ __launch_bounds__(NW * 64) void prefix_kernel(const PrefixParams p) {
   using Geo = PrefixGeo<D, NW, RBW>;
   static_assert(NW <= 16, "per-wave slots");
@@ -106,17 +110,27 @@ __global__ __launch_bounds__(NW * 64) void prefix_kernel(const PrefixParams p) {
   const int lane = tid & 63, m16 = lane & 15, kq = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // Workgroup -> (row tile, KV head, partition).  Workgroups that read the same pages (same head
-  // and partition) are Hkv * S apart, so they share an XCD (and its L2) when that is a multiple
-  // of the XCD count.
-  const int S = p.prefix_tokens / p.partition_tokens;
+  // Workgroup -> (row tile, KV head, partition[, sequence]).  Workgroups that read the same
+  // pages (same head, partition and sequence) are a multiple of Hkv apart, so they share an XCD
+  // (and its L2) when Hkv is a multiple of the XCD count.
   int id = blockIdx.x;
-  const int part = id % S;
-  id /= S;
-  const int kvh = id % p.hkv;
-  const int rt = id / p.hkv;
+  int part, kvh, rt, sb = 0;
+  if constexpr (MQ) {
+    kvh = id % p.hkv;
+    id /= p.hkv;
+    sb = id % p.batch;
+    id /= p.batch;
+    part = id % p.max_partitions;
+    rt = id / p.max_partitions;
+  } else {
+    const int S = p.prefix_tokens / p.partition_tokens;
+    part = id % S;
+    id /= S;
+    kvh = id % p.hkv;
+    rt = id / p.hkv;
+  }
   const int t_lo = part * p.partition_tokens, t_hi = t_lo + p.partition_tokens;
-  const int rows = p.batch * p.group;
+  const int rows = MQ ? p.q_tokens * p.group : p.batch * p.group;
   const int ps_mask = (1 << p.page_shift) - 1;
 
   // This lane's query rows (blocks rb < RBW): r = rt * ROWS + (wave * RBW + rb) * 16 + m16.
@@ -130,10 +144,19 @@ __global__ __launch_bounds__(NW * 64) void prefix_kernel(const PrefixParams p) {
     lim[rb] = 0;
     qrow[rb] = -1;
     if (r < rows) {
-      const int b = r / p.group, g = r % p.group;
-      qrow[rb] = int64_t(b) * p.hq + int64_t(kvh) * p.group + g;
-      const int L = p.context_lens[b];
-      if (L > 0 && L <= p.capacity) lim[rb] = min(L, t_hi);
+      const int g = r % p.group;
+      if constexpr (MQ) {
+        const int j = r / p.group;   // the query token
+        qrow[rb] = (int64_t(sb) * p.q_tokens + j) * p.hq + int64_t(kvh) * p.group + g;
+        const int L = p.context_lens[sb];
+        const int Lj = L - p.q_tokens + 1 + j;
+        if (L > 0 && L <= p.capacity && Lj > 0) lim[rb] = min(Lj, t_hi);
+      } else {
+        const int b = r / p.group;
+        qrow[rb] = int64_t(b) * p.hq + int64_t(kvh) * p.group + g;
+        const int L = p.context_lens[b];
+        if (L > 0 && L <= p.capacity) lim[rb] = min(L, t_hi);
+      }
     }
   }
 
@@ -147,13 +170,19 @@ __global__ __launch_bounds__(NW * 64) void prefix_kernel(const PrefixParams p) {
   for (int off = 32; off >= 1; off >>= 1) my_end = max(my_end, __shfl_xor(my_end, off));
   if (lane == 0) sm.wend[wave] = my_end;
 
-  // Stage the ids of all the partition's pages (every one is a prefix page: the partition ends
-  // at or before prefix_tokens), and note the first out-of-range one.  These loads, the lengths
-  // above and the q operands below are in flight together.
+  // Stage the ids of all the partition's pages, and note the first out-of-range one.  Shared
+  // prefix: every one is a prefix page (the partition ends at or before prefix_tokens).  Multi-
+  // query: entries past the table's width stand for tokens no row reaches, and read as page 0.
+  // These loads, the lengths above and the q operands below are in flight together.
   const int n_ids = p.partition_tokens >> p.page_shift;
   int first_bad = kMaxPrefixPageIds;
   for (int i = tid; i < n_ids; i += NW * 64) {
-    int pg = p.prefix_pages[(t_lo >> p.page_shift) + i];
+    const int idx = (t_lo >> p.page_shift) + i;
+    int pg;
+    if constexpr (MQ)
+      pg = idx < p.max_pages ? p.page_table[int64_t(sb) * p.max_pages + idx] : 0;
+    else
+      pg = p.prefix_pages[idx];
     const bool bad_id = pg < 0 || pg >= p.num_pages;
     if (bad_id) pg = 0;   // read page 0 instead; rows that reach this page get NaN
     sm.pid[i] = pg;
@@ -419,18 +448,26 @@ template <int DT, int D>
 hipError_t launch_prefix_t(const PrefixParams& p, hipStream_t stream) {
   constexpr int NW = kPrefixWaves, RBW = kPrefixRowBlocks;
   constexpr int ROWS = PrefixGeo<D, NW, RBW>::ROWS;
+  if (p.q_tokens > 0) {   // multi-query: (row tile, partition, sequence, KV head)
+    const int64_t tiles = (int64_t(p.q_tokens) * p.group + ROWS - 1) / ROWS;
+    const int64_t units = tiles * p.max_partitions * p.batch * p.hkv;
+    if (units == 0) return hipSuccess;
+    hipLaunchKernelGGL((prefix_kernel<DT, D, NW, RBW, true>), dim3(unsigned(units)), dim3(NW * 64),
+                       0, stream, p);
+    return hipGetLastError();
+  }
   const int64_t tiles = (int64_t(p.batch) * p.group + ROWS - 1) / ROWS;
   const int64_t units = tiles * p.hkv * (p.prefix_tokens / p.partition_tokens);
   if (units == 0) return hipSuccess;
-  hipLaunchKernelGGL((prefix_kernel<DT, D, NW, RBW>), dim3(unsigned(units)), dim3(NW * 64), 0,
-                     stream, p);
+  hipLaunchKernelGGL((prefix_kernel<DT, D, NW, RBW, false>), dim3(unsigned(units)), dim3(NW * 64),
+                     0, stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_prefix(const PrefixParams& p, int dtype, int head_dim, hipStream_t stream) {
-  if (p.batch == 0 || p.prefix_tokens == 0) return hipSuccess;
+  if (p.batch == 0 || (p.q_tokens == 0 && p.prefix_tokens == 0)) return hipSuccess;
   switch (dtype) {
     case DT_BF16:
       return head_dim == 64 ? launch_prefix_t<DT_BF16, 64>(p, stream)

@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     for n in names:
         assert hasattr(L.lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True, text=True).stdout
@@ -168,6 +168,23 @@ def test_step_rope_rejections(L):
     assert st(cos=0) == -1
     assert st(kn=0, vn=0) == -1                   # the rotated key must be appended
     assert L.last_error().startswith("pkv_paged_decode_step_rope")
+
+
+def test_multi_query_rejections(L):
+    s = shape(L)
+    def mq(T=4, PT=64, maxp=1, out=FAKE + 0x500000, po=FAKE + 0x600000, sh=s):
+        return L.lib.pkv_paged_decode_multi_query(
+            FAKE, FAKE + 0x100000, FAKE + 0x200000, FAKE + 0x300000, FAKE + 0x400000, T, 0.1, PT,
+            po, FAKE + 0x700000, maxp, out, None, ctypes.byref(sh), None)
+    assert mq(T=0) == -1
+    assert mq(PT=16, maxp=4) == -2               # partition not a multiple of 64
+    assert mq(maxp=0) == -1
+    assert mq(sh=shape(L, dtype=0)) == -2         # f32 has no matrix-core path
+    assert mq(out=0) == -1
+    assert mq(out=FAKE + 0x10) == -1              # out overlaps q ([B, T, Hq, D] = 8 KB)
+    assert mq(po=FAKE + 0x300000) == -1           # partials overlap the page table
+    assert mq(sh=shape(L, batch=0)) == 0
+    assert L.last_error().startswith("pkv_paged_decode_multi_query")
 
 
 def test_workspace_bytes(L):
