@@ -46,8 +46,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=2, help="workload index (default: 2)")
-    ap.add_argument("--path", choices=["step", "split", "single", "cascade"], default="step",
-                    help="cascade: shared-prefix decode (prefix-shared workloads only)")
+    ap.add_argument("--path", choices=["step", "split", "single", "cascade", "multiquery"],
+                    default="step",
+                    help="cascade: shared-prefix decode (prefix-shared workloads only); "
+                         "multiquery: --q-tokens new tokens per sequence, causal")
+    ap.add_argument("--q-tokens", type=int, default=8, help="multiquery: query tokens per sequence")
     ap.add_argument("--partition-tokens", type=int, default=None)
     ap.add_argument("--rope", action="store_true",
                     help="step path: rotate the new key and the query in the same launch "
@@ -82,6 +85,16 @@ def step_bytes(w, partition_tokens, path):
         step = kv + q + out + table + append + 2 * partials + B * 4
     elif path == "step":
         kernel = step = kv + q + out + table + append   # one launch does all of it
+    elif path == "multiquery":
+        # K and V read once per sequence for all its query tokens; q and out per token; each
+        # (sequence, token) row's partials written and read back.
+        T = w.q_tokens
+        Lj = np.maximum(L[:, None] - T + 1 + np.arange(T)[None, :], 0)
+        partials = int((-(-Lj // partition_tokens)).sum()) * Hq * (D + 1) * 4
+        qo = B * T * Hq * D * e
+        kernel = kv + qo + table + partials             # partition launch
+        step = kv + 2 * qo + table + 2 * partials + B * 4   # no append in this step
+        return dict(kv=kv, step=step, kernel=kernel)
     elif path == "cascade":
         # The shared prefix pages are read once: unique KV bytes, plus every partition's partial
         # written and read back by the merge.
@@ -219,9 +232,11 @@ def main():
         k_new = fill_normal((B, Hkv, D), cfg.dtype, w.seed, STREAM_KNEW)
         v_new = fill_normal((B, Hkv, D), cfg.dtype, w.seed, STREAM_VNEW)
         append_lens = (w.context_lens - 1).astype(np.int32)
+    w.q_tokens = args.q_tokens if args.path == "multiquery" else 1
     if args.path == "cascade" and cfg.lengths[0] != "prefix":
         raise SystemExit("--path cascade needs a prefix-shared workload")
-    P = args.partition_tokens or cfg.partition_tokens or (256 if args.path == "cascade" else 512)
+    P = args.partition_tokens or (256 if args.path in ("cascade", "multiquery") else None) or \
+        cfg.partition_tokens or 512
     log(f"workload {cfg.name}: generated in {time.perf_counter() - t_gen:.1f}s, "
         f"{w.logical_tokens()} live tokens, pool {w.k_pool.shape}")
 
@@ -245,6 +260,12 @@ def main():
     pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(R - 1)]
     out = torch.empty_like(q)
     maxp = pkv.partitions_needed(PS, w.page_table.shape[1], P)
+    if args.path == "multiquery":
+        T = args.q_tokens
+        qm = to_device(fill_normal((B, T, Hq, D), cfg.dtype, w.seed, 9), cfg.dtype, dev)
+        outm = torch.empty_like(qm)
+        pom = torch.empty((B, T, Hq, maxp, D), dtype=torch.float32, device=dev)
+        plm = torch.empty((B, T, Hq, maxp), dtype=torch.float32, device=dev)
     po = torch.empty((B, Hq, maxp, D), dtype=torch.float32, device=dev)
     pl = torch.empty((B, Hq, maxp), dtype=torch.float32, device=dev)
     scale = float(w.scale)
@@ -273,10 +294,16 @@ def main():
             if ev is not None:
                 ev[1].record(stream)
             return
-        pkv.paged_kv_append(kn, vn, kp, vp, table, alens)
+        if args.path != "multiquery":   # the multi-query rows' K/V are already in the pages
+            pkv.paged_kv_append(kn, vn, kp, vp, table, alens)
         if ev is not None:
             ev[0].record(stream)
-        if args.path == "cascade":
+        if args.path == "multiquery":
+            pkv.paged_decode_multi_query(qm, kp, vp, table, lens, P, scale, out=outm,
+                                         partial_out=pom, partial_lse=plm)
+            if ev is not None:
+                ev[1].record(stream)
+        elif args.path == "cascade":
             pkv.paged_decode_cascade(q, kp, vp, prefix_pages, prefix_tokens, table, lens, P, scale,
                                      out=out, partial_out=po, partial_lse=pl)
             if ev is not None:
@@ -323,6 +350,7 @@ def main():
 
     kernel_name = {"split": "decode_kernel (split-KV partial attention)",
                    "cascade": "pkv_paged_decode_cascade (prefix on MFMA + suffix partitions + merge)",
+                   "multiquery": "pkv_paged_decode_multi_query (partitions on MFMA + merge)",
                    "single": "decode_kernel (single pass)",
                    "step": "step_kernel (pkv_paged_decode_step: append + balanced attention + merge)"}[args.path]
     line = {
@@ -342,17 +370,20 @@ def main():
             "workload": cfg.name,
             "description": {"split": "append + split-KV paged decode attention + LSE merge",
                             "cascade": "append + shared-prefix decode: prefix on the matrix cores, suffix partitions, LSE merge",
+                            "multiquery": "causal decode of q_tokens new tokens per sequence (their K/V already paged) on the matrix cores + LSE merge",
                             "single": "append + single-pass paged decode attention",
                             "step": "one decode step in one launch: append, balanced split-KV attention, LSE merge"}[args.path],
             "batch": B, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D, "page_size": PS,
             "context_lens": list(cfg.lengths), "seed": w.seed, "live_tokens": w.logical_tokens(),
-            "partition_tokens": P if args.path in ("split", "cascade") else None, "path": args.path,
+            "partition_tokens": P if args.path in ("split", "cascade", "multiquery") else None,
+            "path": args.path,
             "rope": bool(args.rope),
+            "q_tokens": w.q_tokens,
             "pool_replicas": R,
             "step_bytes": nb["step"], "kv_bytes": nb["kv"],
         },
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
-        "decode_tokens_per_s": round(B / (ms_step * 1e-3), 1),
+        "decode_tokens_per_s": round(B * w.q_tokens / (ms_step * 1e-3), 1),
         "roofline": {
             "kernel": kernel_name,
             "bound": "hbm",

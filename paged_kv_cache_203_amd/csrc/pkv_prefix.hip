@@ -166,6 +166,7 @@ __global__ __launch_bounds__(NW * 64) void prefix_kernel(const PrefixParams p) {
     my_end = max(my_end, lim[rb]);
     lane_min = min(lane_min, lim[rb]);
   }
+  const int my_lim_any = my_end;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) my_end = max(my_end, __shfl_xor(my_end, off));
   if (lane == 0) sm.wend[wave] = my_end;
@@ -301,7 +302,11 @@ __global__ __launch_bounds__(NW * 64) void prefix_kernel(const PrefixParams p) {
     for (int dt = 0; dt < NDT; ++dt) o[rb][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
+  // A wave whose rows all end before the partition only helps load the blocks.
+  const bool wave_active = __ballot(my_lim_any > t_lo) != 0;
+
   auto compute = [&](int n, int bf) {
+    if (!wave_active) return;
     const uint32_t kb = lds_addr(sm.k[bf]);
     const uint32_t vb = lds_addr(sm.vt[bf]);
     const int t0 = t_lo + n * kTB;
@@ -444,17 +449,26 @@ __global__ __launch_bounds__(NW * 64) void prefix_kernel(const PrefixParams p) {
 // Wave layout: kPrefixWaves waves of kPrefixRowBlocks x 16 query rows.
 constexpr int kPrefixWaves = 8, kPrefixRowBlocks = 1;
 
+template <int DT, int D, int NW>
+hipError_t launch_multi_query_t(const PrefixParams& p, hipStream_t stream) {
+  constexpr int ROWS = PrefixGeo<D, NW, 1>::ROWS;
+  const int64_t tiles = (int64_t(p.q_tokens) * p.group + ROWS - 1) / ROWS;
+  const int64_t units = tiles * p.max_partitions * p.batch * p.hkv;
+  if (units == 0) return hipSuccess;
+  hipLaunchKernelGGL((prefix_kernel<DT, D, NW, 1, true>), dim3(unsigned(units)), dim3(NW * 64), 0,
+                     stream, p);
+  return hipGetLastError();
+}
+
 template <int DT, int D>
 hipError_t launch_prefix_t(const PrefixParams& p, hipStream_t stream) {
   constexpr int NW = kPrefixWaves, RBW = kPrefixRowBlocks;
   constexpr int ROWS = PrefixGeo<D, NW, RBW>::ROWS;
   if (p.q_tokens > 0) {   // multi-query: (row tile, partition, sequence, KV head)
-    const int64_t tiles = (int64_t(p.q_tokens) * p.group + ROWS - 1) / ROWS;
-    const int64_t units = tiles * p.max_partitions * p.batch * p.hkv;
-    if (units == 0) return hipSuccess;
-    hipLaunchKernelGGL((prefix_kernel<DT, D, NW, RBW, true>), dim3(unsigned(units)), dim3(NW * 64),
-                       0, stream, p);
-    return hipGetLastError();
+    // Up to 64 rows (G x T): 4-wave workgroups, two per compute unit, so that two blocks of
+    // K/V are in flight per unit; more rows: 8-wave workgroups of 128 rows.
+    if (int64_t(p.q_tokens) * p.group <= 64) return launch_multi_query_t<DT, D, 4>(p, stream);
+    return launch_multi_query_t<DT, D, 8>(p, stream);
   }
   const int64_t tiles = (int64_t(p.batch) * p.group + ROWS - 1) / ROWS;
   const int64_t units = tiles * p.hkv * (p.prefix_tokens / p.partition_tokens);
