@@ -282,6 +282,65 @@ int pkv_validate_metadata(const int32_t* page_table, const int32_t* context_lens
                           int32_t extra_tokens, int32_t check_append_unique,
                           int32_t* device_status, const pkv_shape* shape, void* stream);
 
+/* Whole-page copies in both pools, for copy-on-write: pairs is device int32 [n_pairs][2] of
+ * (source page, destination page); every byte of each source page of k_pool and of v_pool is
+ * copied to the destination page.  Pairs with a page outside [0, num_pages), or a page onto
+ * itself, are skipped.  Destinations must be distinct and must not be sources of other pairs. */
+int pkv_copy_pages(void* k_pool, void* v_pool, const int32_t* pairs, int32_t n_pairs,
+                   const pkv_shape* shape, void* stream);
+
+/* Host page allocator: which physical pages of the pools each sequence uses, with sharing.
+ *
+ * Host memory and host logic only (no device work, no stream).  Pages carry a reference count:
+ * one per sequence that lists the page, one if the prefix cache holds it; a page whose count
+ * reaches zero is free again, and the lowest free id is always taken first, so the ids handed
+ * out depend only on the sequence of calls.  A sequence is a page list plus a token count; its
+ * table row (pkv_pages_seq_table) and length are what the attention calls take as page_table
+ * and context_lens.  This follows the shared page allocator accounting across forked request
+ * sessions (CacheIR page, "Current Capabilities"), page-table-shaped KV allocation and a radix
+ * prefix tree with prefix-cache lookup (TorchInferno page, "Runtime Scaffolds": runtime.paged,
+ * runtime.prefix, runtime.prefix_cache).  Every call returns a PKV_* code; messages come from
+ * pkv_pages_last_error().  One allocator must not be used from two threads at once. */
+typedef struct pkv_page_allocator pkv_page_allocator;
+
+/* A pool of num_pages pages of page_size tokens; NULL on bad arguments. */
+pkv_page_allocator* pkv_pages_create(int32_t num_pages, int32_t page_size);
+void pkv_pages_destroy(pkv_page_allocator* a);
+int32_t pkv_pages_free_count(const pkv_page_allocator* a);
+/* A page's reference count (-1 for a bad page id). */
+int32_t pkv_pages_refcount(const pkv_page_allocator* a, int32_t page);
+/* An empty sequence. */
+int pkv_pages_seq_create(pkv_page_allocator* a, int32_t* seq_out);
+/* A new sequence sharing every page of src, with src's length (a forked request). */
+int pkv_pages_seq_fork(pkv_page_allocator* a, int32_t src, int32_t* seq_out);
+/* Drop the sequence's references; its id may be reused. */
+int pkv_pages_seq_release(pkv_page_allocator* a, int32_t seq);
+/* Grow the sequence by n_tokens (their slots are [length, length + n_tokens), to be written by
+ * an append).  If the last page is partly filled and shared, it is first replaced by a fresh page
+ * and (old, fresh) is written to copies_out (room for max_copies pairs; *n_copies = 1): the
+ * caller copies that page on the device (pkv_copy_pages) before appending.  New pages are taken
+ * for the rest.  Without enough free pages nothing changes and PKV_EWORKSPACE is returned. */
+int pkv_pages_seq_reserve(pkv_page_allocator* a, int32_t seq, int32_t n_tokens,
+                          int32_t* copies_out, int32_t max_copies, int32_t* n_copies);
+int pkv_pages_seq_length(const pkv_page_allocator* a, int32_t seq, int32_t* len_out);
+/* The sequence's page-table row: its page ids, then -1 up to max_pages (PKV_EWORKSPACE if it has
+ * more pages); *n_pages = its page count. */
+int pkv_pages_seq_table(const pkv_page_allocator* a, int32_t seq, int32_t* row,
+                        int32_t max_pages, int32_t* n_pages);
+/* Register the sequence's first n_tokens (token ids) in the prefix cache, page by page: each
+ * full page becomes a node (parent node, its page_size token ids) holding a reference to the
+ * page, unless an equal node exists. */
+int pkv_pages_prefix_insert(pkv_page_allocator* a, int32_t seq, const int32_t* tokens,
+                            int32_t n_tokens);
+/* A new sequence starting on the pages of the longest cached prefix of tokens (whole pages,
+ * token ids compared exactly); *matched_tokens = its length. */
+int pkv_pages_seq_create_with_prefix(pkv_page_allocator* a, const int32_t* tokens,
+                                     int32_t n_tokens, int32_t* seq_out,
+                                     int32_t* matched_tokens);
+/* Evict up to max_pages cache nodes: least recently used leaves whose page only the cache holds. */
+int pkv_pages_prefix_evict(pkv_page_allocator* a, int32_t max_pages, int32_t* evicted);
+const char* pkv_pages_last_error(void);
+
 /* Bytes of partial_out plus partial_lse for `max_partitions` partitions (0 on a bad shape). */
 size_t pkv_partial_workspace_bytes(const pkv_shape* shape, int32_t max_partitions);
 

@@ -11,3 +11,4 @@ from .paged_attention import (to_f64, gather_rows, paged_decode_attention,  # no
                               paged_kv_append, validate_metadata, STATUS_PAGE_RANGE,
                               STATUS_CAPACITY, STATUS_APPEND_ALIAS)
 from . import rope  # noqa: F401,E402
+from . import pages  # noqa: F401,E402

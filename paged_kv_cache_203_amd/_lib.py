@@ -65,6 +65,24 @@ _SIGNATURES = {
     "pkv_paged_decode_multi_query": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, ctypes.c_float,
                                                     _i32, _vp, _vp, _i32, _vp, _vp,
                                                     ctypes.POINTER(PkvShape), _vp]),
+    "pkv_copy_pages": (ctypes.c_int, [_vp, _vp, _vp, _i32, ctypes.POINTER(PkvShape), _vp]),
+    "pkv_pages_create": (_vp, [_i32, _i32]),
+    "pkv_pages_destroy": (None, [_vp]),
+    "pkv_pages_free_count": (_i32, [_vp]),
+    "pkv_pages_refcount": (_i32, [_vp, _i32]),
+    "pkv_pages_seq_create": (ctypes.c_int, [_vp, ctypes.POINTER(_i32)]),
+    "pkv_pages_seq_fork": (ctypes.c_int, [_vp, _i32, ctypes.POINTER(_i32)]),
+    "pkv_pages_seq_release": (ctypes.c_int, [_vp, _i32]),
+    "pkv_pages_seq_reserve": (ctypes.c_int, [_vp, _i32, _i32, ctypes.POINTER(_i32), _i32,
+                                             ctypes.POINTER(_i32)]),
+    "pkv_pages_seq_length": (ctypes.c_int, [_vp, _i32, ctypes.POINTER(_i32)]),
+    "pkv_pages_seq_table": (ctypes.c_int, [_vp, _i32, ctypes.POINTER(_i32), _i32,
+                                           ctypes.POINTER(_i32)]),
+    "pkv_pages_prefix_insert": (ctypes.c_int, [_vp, _i32, ctypes.POINTER(_i32), _i32]),
+    "pkv_pages_seq_create_with_prefix": (ctypes.c_int, [_vp, ctypes.POINTER(_i32), _i32,
+                                                        ctypes.POINTER(_i32), ctypes.POINTER(_i32)]),
+    "pkv_pages_prefix_evict": (ctypes.c_int, [_vp, _i32, ctypes.POINTER(_i32)]),
+    "pkv_pages_last_error": (ctypes.c_char_p, []),
     "pkv_decode_step_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(PkvShape)]),
     "pkv_partial_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(PkvShape), _i32]),
     "pkv_last_error": (ctypes.c_char_p, []),
@@ -464,3 +482,99 @@ def partial_workspace_bytes(batch, num_q_heads, head_dim, max_partitions, page_s
                             max_pages_per_seq=1) -> int:
     s = make_shape(batch, num_q_heads, num_q_heads, head_dim, page_size, 1, max_pages_per_seq, PKV_F32)
     return int(lib.pkv_partial_workspace_bytes(ctypes.byref(s), int(max_partitions)))
+
+
+# ----------------------------------------------------------------------------------------------
+# host page allocator
+# ----------------------------------------------------------------------------------------------
+
+def copy_pages(k_pool, v_pool, pairs) -> None:
+    """Copy whole pages in both pools: ``pairs`` is a device int32 ``[n, 2]`` of (src, dst)."""
+    torch = _torch()
+    _require(k_pool, "k_pool", ndim=4)
+    _require(v_pool, "v_pool", dtype=k_pool.dtype, ndim=4, device=k_pool.device)
+    _require(pairs, "pairs", dtype=torch.int32, ndim=2, device=k_pool.device)
+    NP, PS, Hkv, D = k_pool.shape
+    s = make_shape(0, Hkv, Hkv, D, PS, NP, 1, _dtype_code(k_pool))
+    _check(lib.pkv_copy_pages(k_pool.data_ptr(), v_pool.data_ptr(), pairs.data_ptr(),
+                              int(pairs.shape[0]), ctypes.byref(s), _stream(k_pool.device)))
+
+
+def _page_check(rc: int) -> None:
+    if rc != PKV_OK:
+        raise PkvError(rc, lib.pkv_pages_last_error().decode())
+
+
+class PageAllocator:
+    """The library's host page allocator (reference-counted pages, forks, copy-on-write growth,
+    prefix cache); see ``pkv_pages_*`` in include/pkv.h."""
+
+    def __init__(self, num_pages: int, page_size: int):
+        self._h = lib.pkv_pages_create(int(num_pages), int(page_size))
+        if not self._h:
+            raise PkvError(PKV_EINVAL, lib.pkv_pages_last_error().decode())
+        self.page_size = page_size
+
+    def close(self):
+        if self._h:
+            lib.pkv_pages_destroy(self._h)
+            self._h = None
+
+    __del__ = close
+
+    def free_count(self) -> int:
+        return int(lib.pkv_pages_free_count(self._h))
+
+    def refcount(self, page: int) -> int:
+        return int(lib.pkv_pages_refcount(self._h, int(page)))
+
+    def create(self) -> int:
+        out = _i32()
+        _page_check(lib.pkv_pages_seq_create(self._h, ctypes.byref(out)))
+        return out.value
+
+    def fork(self, seq: int) -> int:
+        out = _i32()
+        _page_check(lib.pkv_pages_seq_fork(self._h, int(seq), ctypes.byref(out)))
+        return out.value
+
+    def release(self, seq: int) -> None:
+        _page_check(lib.pkv_pages_seq_release(self._h, int(seq)))
+
+    def reserve(self, seq: int, n_tokens: int):
+        """Grow by n_tokens; returns the (src, dst) page copies to run before appending."""
+        buf = (_i32 * 2)()
+        n = _i32()
+        _page_check(lib.pkv_pages_seq_reserve(self._h, int(seq), int(n_tokens), buf, 1,
+                                              ctypes.byref(n)))
+        return [(buf[0], buf[1])] if n.value else []
+
+    def length(self, seq: int) -> int:
+        out = _i32()
+        _page_check(lib.pkv_pages_seq_length(self._h, int(seq), ctypes.byref(out)))
+        return out.value
+
+    def table(self, seq: int, max_pages: Optional[int] = None):
+        n = _i32()
+        if max_pages is None:
+            lib.pkv_pages_seq_table(self._h, int(seq), (_i32 * 1)(), 0, ctypes.byref(n))
+            max_pages = n.value
+        row = (_i32 * max(max_pages, 1))()
+        _page_check(lib.pkv_pages_seq_table(self._h, int(seq), row, int(max_pages), ctypes.byref(n)))
+        return list(row[:max_pages])
+
+    def prefix_insert(self, seq: int, tokens) -> None:
+        arr = (_i32 * max(len(tokens), 1))(*tokens)
+        _page_check(lib.pkv_pages_prefix_insert(self._h, int(seq), arr, len(tokens)))
+
+    def create_with_prefix(self, tokens):
+        arr = (_i32 * max(len(tokens), 1))(*tokens)
+        sid, matched = _i32(), _i32()
+        _page_check(lib.pkv_pages_seq_create_with_prefix(self._h, arr, len(tokens),
+                                                         ctypes.byref(sid), ctypes.byref(matched)))
+        return sid.value, matched.value
+
+    def evict(self, max_pages: int) -> int:
+        out = _i32()
+        _page_check(lib.pkv_pages_prefix_evict(self._h, int(max_pages), ctypes.byref(out)))
+        return out.value

@@ -31,7 +31,7 @@ HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", os.path.join(ROOT, "include")]
 
 HIP_SOURCES = ["pkv_kernels.hip", "pkv_prefix.hip", "pkv_rope.hip", "pkv_api.hip"]
-HOST_SOURCES = ["pkv_check.cpp"]
+HOST_SOURCES = ["pkv_check.cpp", "pkv_pages.cpp"]
 
 
 def _run(cmd, verbose):

@@ -418,6 +418,23 @@ int pkv_rope_kv_append(const void* q, const void* k_new, const void* v_new, void
                        "pkv_rope_kv_append");
 }
 
+int pkv_copy_pages(void* k_pool, void* v_pool, const int32_t* pairs, int32_t n_pairs,
+                   const pkv_shape* shape, void* stream) {
+  std::string msg;
+  const int rc = pkv::check_copy_pages(k_pool, v_pool, pairs, n_pairs, shape, msg);
+  if (rc) return set_error(rc, "pkv_copy_pages: " + msg);
+  pkv::CopyPagesParams p{};
+  p.k_pool = k_pool;
+  p.v_pool = v_pool;
+  p.pairs = pairs;
+  p.n = n_pairs;
+  p.num_pages = shape->num_pages;
+  p.page_bytes = int64_t(shape->page_size) * shape->num_kv_heads * shape->head_dim *
+                 pkv::elem_bytes(shape->dtype);
+  (void)hipGetLastError();
+  return launch_status(pkv::launch_copy_pages(p, static_cast<hipStream_t>(stream)), "pkv_copy_pages");
+}
+
 int pkv_validate_metadata(const int32_t* page_table, const int32_t* context_lens,
                           int32_t extra_tokens, int32_t check_append_unique,
                           int32_t* device_status, const pkv_shape* shape, void* stream) {

@@ -405,6 +405,25 @@ int check_rope_append(const void* q, const void* k_new, const void* v_new, const
   return PKV_OK;
 }
 
+int check_copy_pages(const void* k_pool, const void* v_pool, const int32_t* pairs,
+                     int32_t n_pairs, const pkv_shape* s, std::string& msg) {
+  int rc = check_shape(s, msg);
+  if (rc) return rc;
+  if (n_pairs < 0) return fail(msg, PKV_EINVAL, "n_pairs must be >= 0");
+  if (n_pairs == 0) return PKV_OK;
+  if (!k_pool || !v_pool || !pairs)
+    return fail(msg, PKV_EINVAL, "k_pool, v_pool and pairs must be non-NULL");
+  if (!aligned(k_pool, 16) || !aligned(v_pool, 16))
+    return fail(msg, PKV_EUNSUPPORTED, "the pools must be 16-byte aligned");
+  if (!aligned(pairs, 4)) return fail(msg, PKV_EINVAL, "pairs must be 4-byte aligned");
+  const Extents x = extents(*s);
+  if (overlaps(k_pool, x.pool, v_pool, x.pool)) return fail(msg, PKV_EINVAL, "k_pool overlaps v_pool");
+  const uint64_t pn = uint64_t(n_pairs) * 8;
+  if (overlaps(pairs, pn, k_pool, x.pool) || overlaps(pairs, pn, v_pool, x.pool))
+    return fail(msg, PKV_EINVAL, "pairs overlap a pool");
+  return PKV_OK;
+}
+
 int check_validate(const int32_t* page_table, const int32_t* context_lens, int32_t extra_tokens,
                    const int32_t* device_status, const pkv_shape* s, std::string& msg) {
   int rc = check_shape(s, msg);

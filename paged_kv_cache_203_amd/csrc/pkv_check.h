@@ -95,6 +95,9 @@ int check_step(const void* q, const void* k_new, const void* v_new, const void* 
                float scale, const void* workspace, size_t workspace_bytes, uint64_t needed,
                const void* out, const float* lse_out, const pkv_shape* s, std::string& msg);
 
+int check_copy_pages(const void* k_pool, const void* v_pool, const int32_t* pairs,
+                     int32_t n_pairs, const pkv_shape* s, std::string& msg);
+
 int check_validate(const int32_t* page_table, const int32_t* context_lens, int32_t extra_tokens,
                    const int32_t* device_status, const pkv_shape* s, std::string& msg);
 

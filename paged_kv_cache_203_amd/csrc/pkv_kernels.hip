@@ -1051,6 +1051,20 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendParams p) {
   }
 }
 
+// One workgroup per (source, destination) page pair: both pools' pages copied with 16-byte loads
+// and stores.  Pairs naming a page outside the pool, or a page onto itself, are skipped.
+__global__ __launch_bounds__(256) void copy_pages_kernel(const CopyPagesParams p) {
+  const int src = p.pairs[2 * blockIdx.x], dst = p.pairs[2 * blockIdx.x + 1];
+  if (src < 0 || src >= p.num_pages || dst < 0 || dst >= p.num_pages || src == dst) return;
+  const int64_t s0 = int64_t(src) * p.page_bytes, d0 = int64_t(dst) * p.page_bytes;
+  for (int64_t i = threadIdx.x; i < p.page_bytes / 16; i += blockDim.x) {
+    const u32x4 k = *reinterpret_cast<const u32x4*>(static_cast<const char*>(p.k_pool) + s0 + 16 * i);
+    const u32x4 v = *reinterpret_cast<const u32x4*>(static_cast<const char*>(p.v_pool) + s0 + 16 * i);
+    *reinterpret_cast<u32x4*>(static_cast<char*>(p.k_pool) + d0 + 16 * i) = k;
+    *reinterpret_cast<u32x4*>(static_cast<char*>(p.v_pool) + d0 + 16 * i) = v;
+  }
+}
+
 // One workgroup checks every row and writes the status word (no pre-clearing needed).
 __global__ __launch_bounds__(1024) void validate_kernel(const ValidateParams p) {
   __shared__ int status;
@@ -1196,6 +1210,12 @@ hipError_t launch_merge(const MergeParams& p, int dtype, int head_dim, hipStream
 hipError_t launch_append(const AppendParams& p, hipStream_t stream) {
   if (p.batch == 0) return hipSuccess;
   hipLaunchKernelGGL(append_kernel, dim3(unsigned(p.batch)), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_pages(const CopyPagesParams& p, hipStream_t stream) {
+  if (p.n == 0) return hipSuccess;
+  hipLaunchKernelGGL(copy_pages_kernel, dim3(unsigned(p.n)), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -112,6 +112,15 @@ struct RopeParams {
   int32_t rope_rows, hq, hkv;
 };
 
+// Whole-page copies in both pools (copy-on-write of shared pages): pairs [n][2] = (src, dst).
+struct CopyPagesParams {
+  void* k_pool;
+  void* v_pool;
+  const int32_t* pairs;
+  int32_t n, num_pages;
+  int64_t page_bytes;
+};
+
 struct ValidateParams {
   const int32_t* page_table;
   const int32_t* context_lens;
@@ -132,5 +141,6 @@ hipError_t launch_prefix(const PrefixParams& p, int dtype, int head_dim, hipStre
 hipError_t launch_append(const AppendParams& p, hipStream_t stream);
 hipError_t launch_rope_append(const RopeParams& p, int dtype, int head_dim, hipStream_t stream);
 hipError_t launch_validate(const ValidateParams& p, hipStream_t stream);
+hipError_t launch_copy_pages(const CopyPagesParams& p, hipStream_t stream);
 
 }  // namespace pkv
