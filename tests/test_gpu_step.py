@@ -226,3 +226,33 @@ def test_step_shapes(pkv, Hkv, G, D, PS, dtype, Lmax):
     ref, ref_lse = oracle_for(w, pools)
     assert_parity(to_f64(out), ref, dtype, cfg.name)
     assert np.abs(lse.double().cpu().numpy() - ref_lse).max() <= 1e-4
+
+
+def test_step_graph_replays_match_eager(pkv):
+    """The step captured in a HIP graph: every replay, with eager work and synchronisations in
+    between, gives the eager call's output bit for bit (the step allocates nothing and leaves its
+    workspace counters at zero)."""
+    w = W.make_workload(W.config(2).scaled(batch=24, lengths=("uniform", 1, 1500)))
+    d = DeviceWorkload(w)
+    k_new, v_new, alens = with_new_rows(w)
+    kn, vn = to_device(k_new, w.dtype), to_device(v_new, w.dtype)
+    lens = torch.from_numpy(alens).cuda()
+    ws = torch.zeros(pkv.decode_step_workspace_bytes(d.q, d.k_pool, d.page_table),
+                     dtype=torch.uint8, device="cuda")
+    eager = pkv.paged_decode_step(d.q, d.k_pool, d.v_pool, d.page_table, lens, d.scale,
+                                  k_new=kn, v_new=vn, workspace=ws)
+    torch.cuda.synchronize()
+    out = torch.empty_like(eager)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        pkv.paged_decode_step(d.q, d.k_pool, d.v_pool, d.page_table, lens, d.scale, k_new=kn,
+                              v_new=vn, out=out, workspace=ws)
+    other = DeviceWorkload(W.make_workload(W.config(2).scaled(batch=5, lengths=("uniform", 1, 300))))
+    for i in range(6):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {i}"
+        pkv.paged_decode_step(other.q, other.k_pool, other.v_pool, other.page_table,
+                              other.context_lens, other.scale)        # eager work in between
+        torch.cuda.synchronize()
