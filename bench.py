@@ -235,7 +235,7 @@ def main():
     w.q_tokens = args.q_tokens if args.path == "multiquery" else 1
     if args.path == "cascade" and cfg.lengths[0] != "prefix":
         raise SystemExit("--path cascade needs a prefix-shared workload")
-    P = args.partition_tokens or (256 if args.path in ("cascade", "multiquery") else None) or \
+    P = args.partition_tokens or {"cascade": 256, "multiquery": 1024}.get(args.path) or \
         cfg.partition_tokens or 512
     log(f"workload {cfg.name}: generated in {time.perf_counter() - t_gen:.1f}s, "
         f"{w.logical_tokens()} live tokens, pool {w.k_pool.shape}")

@@ -317,7 +317,7 @@ def paged_decode_cascade(q, k_pool, v_pool, prefix_pages, prefix_tokens: int, pa
     return out
 
 
-def paged_decode_multi_query(q, k_pool, v_pool, page_table, context_lens, partition_tokens: int = 256,
+def paged_decode_multi_query(q, k_pool, v_pool, page_table, context_lens, partition_tokens: int = 1024,
                              scale: Optional[float] = None, out=None, lse_out=None,
                              partial_out=None, partial_lse=None):
     """Causal decode of T new tokens per sequence: ``q [B, T, Hq, D]``; ``context_lens[b]``
