@@ -401,6 +401,8 @@ def main():
         },
         "cpu_baseline": cpu,
         "device": torch.cuda.get_device_name(0),
+        "gfx_arch": getattr(torch.cuda.get_device_properties(0), "gcnArchName", None),
+        "hip": getattr(torch.version, "hip", None),
         "torch": torch.__version__,
         "lib": pkv.version(),
     }
