@@ -368,15 +368,18 @@ struct HeadPipe {
 
   // Stream all of this wave's tiles of `s`.  With has_next, the loads of the next run()'s q and
   // first page ids (for `next`) start as the last chunk begins (see prefetch).  When prefetch() ran for `s`,
-  // its q is taken here and its first page ids are used.
+  // its q is taken here and its first page ids are used.  `at_start` runs once per call, on
+  // every wave, after all of this wave's earlier memory operations have completed and before
+  // any load of `s`'s tiles is issued.
   // lockstep: every wave of the workgroup streams the same tile list (one wave per KV head); a
   // barrier per round of DEPTH tiles then keeps the waves together, so that the rows of all
   // heads of a token are read close in time and no wave falls behind the others.
   __device__ void run(const HeadSource& s, float scale_log2, int G) {
-    run(s, scale_log2, G, s, false, false);
+    run(s, scale_log2, G, s, false, false, [] {});
   }
+  template <class AtStart>
   __device__ void run(const HeadSource& s, float scale_log2, int G, const HeadSource& next,
-                      bool has_next, bool lockstep) {
+                      bool has_next, bool lockstep, AtStart&& at_start) {
     const int n_my = tiles_of(s);
     const bool had_pref = pref_ready;
     if (pref_ready) {
@@ -392,6 +395,7 @@ struct HeadPipe {
       // The page ids (and anything older) have landed before the next piece's prefetch is
       // issued, so no later wait for them can also wait for the prefetch.
       wait_vmcnt<0>();
+      if (c0 == 0) at_start();
       if (has_next && c0 + kChunk >= n_my) prefetch(next, G);   // the last chunk
       auto page_at = [&](int k) { return __builtin_amdgcn_readlane(page_vec, min(k, nc - 1)); };
       auto tile_at = [&](int k) { return s.sub + (c0 + min(k, nc - 1)) * s.stride; };
@@ -427,7 +431,11 @@ struct HeadPipe {
       }
       wait_vmcnt<0>();   // nothing is in flight here; this states it for the next chunk
     }
-    if (has_next && n_my == 0) prefetch(next, G);   // no tiles of `s` for this wave
+    if (n_my == 0) {   // no tiles of `s` for this wave
+      wait_vmcnt<0>();
+      at_start();
+      if (has_next) prefetch(next, G);
+    }
   }
 
   // Reduce the wave's state across its 4 row groups and store it at `ep` (LDS):
@@ -899,6 +907,21 @@ __global__ __launch_bounds__(NW * 64) void step_kernel(const StepParams p) {
 
   // Each piece's q and first page ids are loaded while the previous piece drains; the first
   // piece's q and page ids load together.
+  // The range's first piece, when split, is counted as soon as the next piece starts: every wave
+  // has then waited for its own stores, and the barrier (the waves reach it together) makes that
+  // true of the whole partial.  Its result is read at the end of the range.  A range's first
+  // piece is the tail of a sequence whose other pieces end at the end of their ranges, so the
+  // count almost never comes in last, and the workgroup that finishes a range rarely has two
+  // merges to do.
+  int early_b = -1, early_tiles = 0, early_ret = 0;
+  auto count_first = [&] {
+    if (early_b < 0 || early_tiles == 0) return;
+    __syncthreads();   // every wave's partial stores have completed
+    if (threadIdx.x == 0)
+      early_ret = __hip_atomic_fetch_add(&p.ws_count[int64_t(early_b) * nhg + hg], early_tiles,
+                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    early_tiles = 0;
+  };
   HeadSource cur = source(b);
   hp.prefetch(cur, G);
   while (true) {
@@ -906,7 +929,7 @@ __global__ __launch_bounds__(NW * 64) void step_kernel(const StepParams p) {
     const bool has_next = nb < B;
     const HeadSource nxt = source(has_next ? nb : b);
     hp.reset();
-    hp.run(cur, a.scale_log2, G, nxt, has_next, WPH == 1);
+    hp.run(cur, a.scale_log2, G, nxt, has_next, WPH == 1, count_first);
 
     const int n_b = prefix(b + 1) - prefix(b);
     const int tb = max(lo, prefix(b)) - prefix(b);
@@ -950,6 +973,7 @@ __global__ __launch_bounds__(NW * 64) void step_kernel(const StepParams p) {
       if (tb > 0) {
         split_first = b;
         first_tiles = te - tb;
+        early_b = b, early_tiles = first_tiles;
       } else {
         split_last = b;
         last_tiles = te - tb;
@@ -960,9 +984,9 @@ __global__ __launch_bounds__(NW * 64) void step_kernel(const StepParams p) {
     cur = nxt;
   }
 
-  // Count the split pieces' tiles in (at most two pieces: the range's first and last); the
-  // workgroup that brings a sequence's count to its number of tiles merges all of its pieces.  This is deferred to the end of
-  // the range so that no workgroup stalls between pieces.  The partials were written, and are
+  // Count the split pieces' tiles in (at most two pieces: the range's first and last; the first
+  // one was usually counted already, see count_first); the workgroup that brings a sequence's
+  // count to its number of tiles merges all of its pieces.  The partials were written, and are
   // read, with device-scope accesses, which are coherent across the XCDs (each has its own L2)
   // without an L2 write-back or invalidate: each thread waits until its stores are complete,
   // the barrier orders that before the increments, and a merging workgroup issues its loads
@@ -975,8 +999,10 @@ __global__ __launch_bounds__(NW * 64) void step_kernel(const StepParams p) {
     const int tiles = threadIdx.x == 0 ? first_tiles : last_tiles;
     int last = 0;
     if (sb >= 0) {
-      const int old = __hip_atomic_fetch_add(&p.ws_count[int64_t(sb) * nhg + hg], tiles,
-                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const bool counted = threadIdx.x == 0 && early_b == sb && early_tiles == 0;
+      const int old = counted ? early_ret
+                              : __hip_atomic_fetch_add(&p.ws_count[int64_t(sb) * nhg + hg], tiles,
+                                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       last = old + tiles == prefix(sb + 1) - prefix(sb);
     }
     merging[threadIdx.x] = last;
