@@ -316,9 +316,9 @@ int check_step(const void* q, const void* k_new, const void* v_new, const void* 
   if (s->num_q_heads > kMaxStepHeads)
     return fail(msg, PKV_EUNSUPPORTED, "num_q_heads must be <= 1024 for the decode step");
   {
-    // The step's work split counts 4 units per 16-token tile plus 8 per sequence in int32.
+    // The step's work split counts 4 units per 16-token tile plus up to 24 per sequence in int32.
     const int64_t tiles = (int64_t(s->max_pages_per_seq) * s->page_size + 1 + 15) / 16;
-    if (int64_t(s->batch) * (4 * tiles + 8) >= (int64_t(1) << 31))
+    if (int64_t(s->batch) * (4 * tiles + 24) >= (int64_t(1) << 31))
       return fail(msg, PKV_EUNSUPPORTED, "batch * page-table capacity too large for the decode step");
   }
   if (s->batch == 0) return PKV_OK;

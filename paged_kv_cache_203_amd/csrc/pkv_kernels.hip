@@ -606,52 +606,67 @@ __device__ inline int step_tiles(const StepParams& p, int b) {
 }
 
 // The split of a step's work over the workgroup ranges.  Every sequence b weighs 4 units per
-// tile plus kStartUnits for its start: a range that starts a new sequence pays one pipeline
-// drain and refill, so it gets that much less streaming.  `wpre` is the exclusive prefix of the
-// weights (B + 1 entries, in LDS); the `groups` ranges cut the weighted line [0, WT) evenly,
-// and a range owns the tiles whose weighted start falls in it.  Everything depends on the
-// lengths only.
-constexpr int kStartUnits = 8;   // two tiles
+// tile plus `su` start units: a range that starts a new sequence pays one pipeline drain and
+// refill, so it gets that much less streaming.  `wpre` is the exclusive prefix of the weights
+// (B + 1 entries, in LDS); the `groups` ranges cut the weighted line [0, WT) evenly, and a range
+// owns the tiles whose weighted start falls in it.  Everything depends on the lengths only.
+// The start weight was measured: three tiles when each wave streams a whole KV head (12 units:
+// 113.5 us for the Llama-3-8B-shaped step, against 115.5 us at 8 and 118 us at 4), six when
+// several waves take turns on one head's tiles and so each restarts on fewer of them (24 units:
+// 57.8 us for the Qwen2-7B-shaped step, against 65.5 us at 8).
+__device__ inline int start_units(int waves_per_head) { return waves_per_head == 1 ? 12 : 24; }
 
 struct StepSplit {
   const int* wpre;
   int B;
   int64_t WT, groups;
+  int su;   // start units per sequence
 
   // Tiles of the sequences before b (the exclusive tile prefix).
-  __device__ int tiles_before(int b) const { return (wpre[b] - kStartUnits * b) >> 2; }
+  __device__ int tiles_before(int b) const { return (wpre[b] - su * b) >> 2; }
   __device__ int total_tiles() const { return tiles_before(B); }
   __device__ int64_t bound(int64_t w) const { return w * WT / groups; }
 
-  // The last b in [0, B] with wpre[b] <= x.
-  __device__ int seq_at(int64_t x) const {
+  // The last b in [0, B] with f(b) <= x, for f nondecreasing with f(0) <= x: up to
+  // kParallelSearch entries are compared by the wave's lanes at once (the count of b in [1, B]
+  // with f(b) <= x), longer batches are bisected.
+  static constexpr int kParallelSearch = 256;
+  template <class F>
+  __device__ int last_le(F f, int64_t x) const {
+    if (B <= kParallelSearch) {
+      const int lane = threadIdx.x & 63;
+      int c = 0;
+      for (int i0 = 1; i0 <= B; i0 += 64) {
+        const uint64_t m = __ballot(i0 + lane <= B && f(i0 + lane) <= x);
+        c += __popcll(m);
+        if (~m != 0) break;
+      }
+      return c;
+    }
     int l = 0, r = B + 1;
     while (r - l > 1) {
       const int m = (l + r) >> 1;
-      if (wpre[m] <= x) l = m; else r = m;
+      if (f(m) <= x) l = m; else r = m;
     }
     return l;
   }
+  // The last b in [0, B] with wpre[b] <= x.
+  __device__ int seq_at(int64_t x) const { return last_le([&](int b) { return int64_t(wpre[b]); }, x); }
   // The sequence holding tile t (tiles_before(b) <= t < tiles_before(b + 1)).
   __device__ int seq_of_tile(int t) const {
-    int l = 0, r = B + 1;
-    while (r - l > 1) {
-      const int m = (l + r) >> 1;
-      if (tiles_before(m) <= t) l = m; else r = m;
-    }
-    return l;
+    return last_le([&](int b) { return int64_t(tiles_before(b)); }, t);
   }
-  // The first tile whose weighted start (wpre[b] + kStartUnits + 4 k for tile k of b) is >= x.
+  // The first tile whose weighted start (wpre[b] + su + 4 k for tile k of b) is >= x.
   __device__ int first_tile_at(int64_t x) const {
     const int b = seq_at(x);
     if (b >= B) return total_tiles();
-    const int64_t o = x - wpre[b] - kStartUnits;
+    const int64_t o = x - wpre[b] - su;
     const int t0 = tiles_before(b);
     const int k = o <= 0 ? 0 : int((o + 3) >> 2);
     return min(t0 + k, tiles_before(b + 1));
   }
   __device__ int range_lo(int64_t w) const { return first_tile_at(bound(w)); }
-  // Within sequence b (n tiles, weighted starts base + 4 k with base = wpre[b] + kStartUnits),
+  // Within sequence b (n tiles, weighted starts base + 4 k with base = wpre[b] + su),
   // no search is needed: the range owning weighted position x, and how many of b's tiles range
   // w holds.
   __device__ int64_t range_of_pos(int64_t x) const { return ((x + 1) * groups - 1) / WT; }
@@ -663,16 +678,16 @@ struct StepSplit {
   }
 };
 
-// Exclusive prefix sum of the weights 4 * step_tiles(b) + kStartUnits over the batch into
-// `wpre` (B + 1 entries).  `scan` is NT ints of scratch.  All threads of the block take part.
+// Exclusive prefix sum of the weights 4 * step_tiles(b) + su over the batch into `wpre`
+// (B + 1 entries).  `scan` is NT ints of scratch.  All threads of the block take part.
 template <int NT>
-__device__ void weight_prefix(const StepParams& p, int* wpre, int* scan) {
+__device__ void weight_prefix(const StepParams& p, int su, int* wpre, int* scan) {
   const int B = p.a.batch;
   const int tid = threadIdx.x;
   const int seg = (B + NT - 1) / NT;
   const int lo = min(B, tid * seg), hi = min(B, lo + seg);
   int local = 0;
-  for (int b = lo; b < hi; ++b) local += 4 * step_tiles(p, b) + kStartUnits;
+  for (int b = lo; b < hi; ++b) local += 4 * step_tiles(p, b) + su;
   scan[tid] = local;
   __syncthreads();
   for (int off = 1; off < NT; off <<= 1) {
@@ -684,7 +699,7 @@ __device__ void weight_prefix(const StepParams& p, int* wpre, int* scan) {
   int run = scan[tid] - local;
   for (int b = lo; b < hi; ++b) {
     wpre[b] = run;
-    run += 4 * step_tiles(p, b) + kStartUnits;
+    run += 4 * step_tiles(p, b) + su;
   }
   if (tid == NT - 1) wpre[B] = scan[NT - 1];
   __syncthreads();
@@ -703,7 +718,7 @@ __device__ void step_merge(const StepParams& p, const StepSplit& sp, int b, int 
   constexpr int kMU = 8, kCols = 2;
   const DecodeParams& a = p.a;
   const int n = E - S;
-  const int64_t base = sp.wpre[b] + kStartUnits;   // weighted start of the sequence's first tile
+  const int64_t base = sp.wpre[b] + sp.su;   // weighted start of the sequence's first tile
   const int64_t w_lo = sp.range_of_pos(base);
   const int npc = int(sp.range_of_pos(base + 4 * int64_t(n - 1)) - w_lo + 1);   // candidate ranges
   if (threadIdx.x < min(npc, NT)) flags[threadIdx.x] = sp.tiles_in(w_lo + threadIdx.x, base, n) > 0;
@@ -795,9 +810,10 @@ __global__ __launch_bounds__(NW * 64) void step_kernel(const StepParams p) {
   int split_first = -1, split_last = -1;   // sequences whose piece here is split
   int first_tiles = 0, last_tiles = 0;      // ... and the tiles of those pieces
 
-  weight_prefix<NW * 64>(p, wpre, scan);
+  const int su = start_units(WPH);
+  weight_prefix<NW * 64>(p, su, wpre, scan);
   const int B = a.batch;
-  const StepSplit sp{wpre, B, wpre[B], p.groups};
+  const StepSplit sp{wpre, B, wpre[B], p.groups, su};
   auto prefix = [&](int x) { return sp.tiles_before(x); };   // tiles of the sequences before x
   // Rows without tiles (padding, or longer than the page table can address): 0 / NaN outputs,
   // written by one workgroup each.
