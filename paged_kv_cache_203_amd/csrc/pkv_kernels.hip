@@ -679,7 +679,8 @@ struct StepSplit {
 };
 
 // Exclusive prefix sum of the weights 4 * step_tiles(b) + su over the batch into `wpre`
-// (B + 1 entries).  `scan` is NT ints of scratch.  All threads of the block take part.
+// (B + 1 entries).  `scan` is NT / 64 ints of scratch (or more).  All threads of the block take
+// part.
 template <int NT>
 __device__ void weight_prefix(const StepParams& p, int su, int* wpre, int* scan) {
   const int B = p.a.batch;
@@ -688,20 +689,26 @@ __device__ void weight_prefix(const StepParams& p, int su, int* wpre, int* scan)
   const int lo = min(B, tid * seg), hi = min(B, lo + seg);
   int local = 0;
   for (int b = lo; b < hi; ++b) local += 4 * step_tiles(p, b) + su;
-  scan[tid] = local;
-  __syncthreads();
-  for (int off = 1; off < NT; off <<= 1) {
-    const int v = scan[tid] + (tid >= off ? scan[tid - off] : 0);
-    __syncthreads();
-    scan[tid] = v;
-    __syncthreads();
+  // Inclusive scan within each wave by shuffles; the waves' totals meet in LDS (one barrier).
+  int incl = local;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(incl, off, 64);
+    if ((tid & 63) >= off) incl += v;
   }
-  int run = scan[tid] - local;
+  if ((tid & 63) == 63) scan[tid >> 6] = incl;
+  __syncthreads();
+  int before = 0, total = 0;
+  for (int wv = 0; wv < NT / 64; ++wv) {
+    before += wv < (tid >> 6) ? scan[wv] : 0;
+    total += scan[wv];
+  }
+  int run = before + incl - local;
   for (int b = lo; b < hi; ++b) {
     wpre[b] = run;
     run += 4 * step_tiles(p, b) + su;
   }
-  if (tid == NT - 1) wpre[B] = scan[NT - 1];
+  if (tid == NT - 1) wpre[B] = total;
   __syncthreads();
 }
 
@@ -721,7 +728,10 @@ __device__ void step_merge(const StepParams& p, const StepSplit& sp, int b, int 
   const int64_t base = sp.wpre[b] + sp.su;   // weighted start of the sequence's first tile
   const int64_t w_lo = sp.range_of_pos(base);
   const int npc = int(sp.range_of_pos(base + 4 * int64_t(n - 1)) - w_lo + 1);   // candidate ranges
-  if (threadIdx.x < min(npc, NT)) flags[threadIdx.x] = sp.tiles_in(w_lo + threadIdx.x, base, n) > 0;
+  // A range at least one tile wide (4 weight units) holds a tile of every sequence it lies inside.
+  const bool dense = sp.WT >= 4 * sp.groups;
+  if (threadIdx.x < min(npc, NT))
+    flags[threadIdx.x] = dense || sp.tiles_in(w_lo + threadIdx.x, base, n) > 0;
   __syncthreads();
   const int ncol = NH * (D / 4);
   // Byte offsets below are relative to the first candidate's partial rows.
@@ -746,7 +756,7 @@ __device__ void step_merge(const StepParams& p, const StepSplit& sp, int b, int 
 #pragma unroll
       for (int u = 0; u < kMU; ++u) {
         const int k = k0 + u;
-        const bool ok = k < npc && (k < NT ? flags[k] != 0 : sp.tiles_in(w_lo + k, base, n) > 0);
+        const bool ok = k < npc && (k < NT ? flags[k] != 0 : dense || sp.tiles_in(w_lo + k, base, n) > 0);
 #pragma unroll
         for (int k = 0; k < kCols; ++k) {
           const int64_t row = int64_t(k0 + u) * a.hq + h[k];
