@@ -728,11 +728,13 @@ __device__ void step_merge(const StepParams& p, const StepSplit& sp, int b, int 
   const int64_t base = sp.wpre[b] + sp.su;   // weighted start of the sequence's first tile
   const int64_t w_lo = sp.range_of_pos(base);
   const int npc = int(sp.range_of_pos(base + 4 * int64_t(n - 1)) - w_lo + 1);   // candidate ranges
-  // A range at least one tile wide (4 weight units) holds a tile of every sequence it lies inside.
+  // A range at least one tile wide (4 weight units) holds a tile of every sequence it lies
+  // inside, so every candidate holds a piece and no flags are needed.
   const bool dense = sp.WT >= 4 * sp.groups;
-  if (threadIdx.x < min(npc, NT))
-    flags[threadIdx.x] = dense || sp.tiles_in(w_lo + threadIdx.x, base, n) > 0;
-  __syncthreads();
+  if (!dense) {
+    if (threadIdx.x < min(npc, NT)) flags[threadIdx.x] = sp.tiles_in(w_lo + threadIdx.x, base, n) > 0;
+    __syncthreads();
+  }
   const int ncol = NH * (D / 4);
   // Byte offsets below are relative to the first candidate's partial rows.
   const int64_t row0 = (w_lo + b) * a.hq;
@@ -756,7 +758,7 @@ __device__ void step_merge(const StepParams& p, const StepSplit& sp, int b, int 
 #pragma unroll
       for (int u = 0; u < kMU; ++u) {
         const int k = k0 + u;
-        const bool ok = k < npc && (k < NT ? flags[k] != 0 : dense || sp.tiles_in(w_lo + k, base, n) > 0);
+        const bool ok = k < npc && (dense || (k < NT ? flags[k] != 0 : sp.tiles_in(w_lo + k, base, n) > 0));
 #pragma unroll
         for (int k = 0; k < kCols; ++k) {
           const int64_t row = int64_t(k0 + u) * a.hq + h[k];
@@ -845,6 +847,45 @@ __global__ __launch_bounds__(NW * 64) void step_kernel(const StepParams p) {
   HeadPipe<DT, D, GP, DEPTH, ROPE> hp;
   hp.init(a.tok_stride, lds_addr(sm.w[wave]), &sm.p[wave][0][0], &sm.a[wave][0]);
 
+  // This wave's source for sequence bb: the tiles of bb in this range, for its KV head.
+  auto source = [&](int bb) {
+    HeadSource src;
+    const int tb = max(lo, prefix(bb)) - prefix(bb);
+    const int te = min(hi, prefix(bb + 1)) - prefix(bb);
+    src.kpool = static_cast<const char*>(a.k_pool);
+    src.vpool = static_cast<const char*>(a.v_pool);
+    src.table = a.page_table + int64_t(bb) * a.max_pages;
+    src.page_shift = a.page_shift;
+    src.num_pages = a.num_pages;
+    src.tok_stride = a.tok_stride;
+    src.page_stride = a.page_stride;
+    src.head_off = kvh * Geo::RB;
+    src.t_begin = tb * kTile;
+    src.t_end = min(a.context_lens[bb] + p.append, te * kTile);
+    src.sub = wave / HPW;
+    src.stride = WPH;
+    src.q_group = static_cast<const char*>(a.q) + (int64_t(bb) * a.hq + int64_t(kvh) * G) * Geo::RB;
+    src.rope_cos = p.rope_cos;
+    src.rope_sin = p.rope_sin;
+    src.rope_pos = -1;
+    if constexpr (ROPE) {
+      const int L = a.context_lens[bb];   // the new token's position
+      src.rope_pos = L >= 0 && L < p.rope_rows ? L : -1;
+    }
+    return src;
+  };
+  // The next sequence after bb with tiles in this range, or B.
+  auto next_seq = [&](int bb) {
+    for (++bb; bb < B && prefix(bb) < hi; ++bb)
+      if (prefix(bb + 1) > prefix(bb)) return bb;
+    return B;
+  };
+
+  // Each piece's q and first page ids are loaded while the previous piece drains; the first
+  // piece's load while the appended rows are written (they read neither the pools nor the rows).
+  HeadSource cur = source(b);
+  hp.prefetch(cur, G);
+
   // The appended rows of every sequence whose last tile lies in this range are written first;
   // the barrier (which waits for the stores) orders them before any load of those tiles.  No
   // other workgroup reads those slots in this step.
@@ -897,42 +938,6 @@ __global__ __launch_bounds__(NW * 64) void step_kernel(const StepParams p) {
     __syncthreads();
   }
 
-  // This wave's source for sequence bb: the tiles of bb in this range, for its KV head.
-  auto source = [&](int bb) {
-    HeadSource src;
-    const int tb = max(lo, prefix(bb)) - prefix(bb);
-    const int te = min(hi, prefix(bb + 1)) - prefix(bb);
-    src.kpool = static_cast<const char*>(a.k_pool);
-    src.vpool = static_cast<const char*>(a.v_pool);
-    src.table = a.page_table + int64_t(bb) * a.max_pages;
-    src.page_shift = a.page_shift;
-    src.num_pages = a.num_pages;
-    src.tok_stride = a.tok_stride;
-    src.page_stride = a.page_stride;
-    src.head_off = kvh * Geo::RB;
-    src.t_begin = tb * kTile;
-    src.t_end = min(a.context_lens[bb] + p.append, te * kTile);
-    src.sub = wave / HPW;
-    src.stride = WPH;
-    src.q_group = static_cast<const char*>(a.q) + (int64_t(bb) * a.hq + int64_t(kvh) * G) * Geo::RB;
-    src.rope_cos = p.rope_cos;
-    src.rope_sin = p.rope_sin;
-    src.rope_pos = -1;
-    if constexpr (ROPE) {
-      const int L = a.context_lens[bb];   // the new token's position
-      src.rope_pos = L >= 0 && L < p.rope_rows ? L : -1;
-    }
-    return src;
-  };
-  // The next sequence after bb with tiles in this range, or B.
-  auto next_seq = [&](int bb) {
-    for (++bb; bb < B && prefix(bb) < hi; ++bb)
-      if (prefix(bb + 1) > prefix(bb)) return bb;
-    return B;
-  };
-
-  // Each piece's q and first page ids are loaded while the previous piece drains; the first
-  // piece's q and page ids load together.
   // The range's first piece, when split, is counted as soon as the next piece starts: every wave
   // has then waited for its own stores, and the barrier (the waves reach it together) makes that
   // true of the whole partial.  Its result is read at the end of the range.  A range's first
@@ -948,8 +953,6 @@ __global__ __launch_bounds__(NW * 64) void step_kernel(const StepParams p) {
                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     early_tiles = 0;
   };
-  HeadSource cur = source(b);
-  hp.prefetch(cur, G);
   while (true) {
     const int nb = next_seq(b);
     const bool has_next = nb < B;
