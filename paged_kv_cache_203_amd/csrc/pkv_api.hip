@@ -298,11 +298,16 @@ int decode_step(const char* name, const void* q, const void* k_new, const void* 
   p.lse_out = lse_out;
   p.groups = int32_t(groups);
   p.append = k_new ? 1 : 0;
+  // Several waves per KV head split its query heads when every wave gets at least one.
+  const int wph = pkv::decode_waves() / p.a.heads_per_wg;
+  const int gw = (p.a.group + wph - 1) / wph;
+  p.qsplit = wph > 1 && (wph - 1) * gw < p.a.group ? 1 : 0;
   p.rope_cos = rope_cos;
   p.rope_sin = rope_sin;
   p.rope_rows = rope_positions;
   (void)hipGetLastError();
-  return launch_status(pkv::launch_step(p, shape->dtype, shape->head_dim, group_pad(p.a.group),
+  return launch_status(pkv::launch_step(p, shape->dtype, shape->head_dim,
+                                        group_pad(p.qsplit ? gw : p.a.group),
                                         static_cast<hipStream_t>(stream)),
                        name);
 }

@@ -817,6 +817,13 @@ __global__ __launch_bounds__(NW * 64) void step_kernel(const StepParams p) {
   const int hg = blockIdx.x % nhg;
   const int w = blockIdx.x / nhg;
   const int kvh = hg * HPW + wave % HPW;
+  // This wave's query heads of the group: gs .. gs + Gw - 1 (all of them unless the waves of a
+  // KV head split them; then every wave streams all of the head's tiles, in lockstep).
+  const bool qsplit = p.qsplit != 0;
+  const int GW = qsplit ? (G + WPH - 1) / WPH : G;
+  const int gs = qsplit ? (wave / HPW) * GW : 0;
+  const int Gw = qsplit ? min(GW, G - gs) : G;
+  const bool own_heads = WPH == 1 || qsplit;   // the wave alone finishes its query heads
 
   __shared__ int merging[2];
   int split_first = -1, split_last = -1;   // sequences whose piece here is split
@@ -862,9 +869,9 @@ __global__ __launch_bounds__(NW * 64) void step_kernel(const StepParams p) {
     src.head_off = kvh * Geo::RB;
     src.t_begin = tb * kTile;
     src.t_end = min(a.context_lens[bb] + p.append, te * kTile);
-    src.sub = wave / HPW;
-    src.stride = WPH;
-    src.q_group = static_cast<const char*>(a.q) + (int64_t(bb) * a.hq + int64_t(kvh) * G) * Geo::RB;
+    src.sub = qsplit ? 0 : wave / HPW;
+    src.stride = qsplit ? 1 : WPH;
+    src.q_group = static_cast<const char*>(a.q) + (int64_t(bb) * a.hq + int64_t(kvh) * G + gs) * Geo::RB;
     src.rope_cos = p.rope_cos;
     src.rope_sin = p.rope_sin;
     src.rope_pos = -1;
@@ -884,7 +891,7 @@ __global__ __launch_bounds__(NW * 64) void step_kernel(const StepParams p) {
   // Each piece's q and first page ids are loaded while the previous piece drains; the first
   // piece's load while the appended rows are written (they read neither the pools nor the rows).
   HeadSource cur = source(b);
-  hp.prefetch(cur, G);
+  hp.prefetch(cur, Gw);
 
   // The appended rows of every sequence whose last tile lies in this range are written first;
   // the barrier (which waits for the stores) orders them before any load of those tiles.  No
@@ -958,17 +965,17 @@ __global__ __launch_bounds__(NW * 64) void step_kernel(const StepParams p) {
     const bool has_next = nb < B;
     const HeadSource nxt = source(has_next ? nb : b);
     hp.reset();
-    hp.run(cur, a.scale_log2, G, nxt, has_next, WPH == 1, count_first);
+    hp.run(cur, a.scale_log2, Gw, nxt, has_next, own_heads, count_first);
 
     const int n_b = prefix(b + 1) - prefix(b);
     const int tb = max(lo, prefix(b)) - prefix(b);
     const int te = min(hi, prefix(b + 1)) - prefix(b);
     const bool whole = tb == 0 && te == n_b;   // this workgroup holds all of the sequence
     const int64_t slot = int64_t(w) + b;
-    if (WPH == 1) {
-      // One wave per KV head: the wave finishes its head from registers, with no barrier.
-      hp.finish_direct(G, [&](int g, int d0, const float (&vals)[Geo::VPL], float lse) {
-        const int h = kvh * G + g;
+    if (own_heads) {
+      // The wave finishes its query heads from registers, with no barrier.
+      hp.finish_direct(Gw, [&](int g, int d0, const float (&vals)[Geo::VPL], float lse) {
+        const int h = kvh * G + gs + g;
         if (whole) {
           store_row<DT, Geo::VPL>(p.out, (int64_t(b) * a.hq + h) * D + d0, vals);
           if (d0 == 0 && p.lse_out) p.lse_out[int64_t(b) * a.hq + h] = lse;

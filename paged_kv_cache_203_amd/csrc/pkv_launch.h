@@ -46,6 +46,10 @@ struct StepParams {
   float* lse_out;        // may be null
   int32_t groups;        // token-range groups per head group
   int32_t append;        // 1: append k_new/v_new at context_lens[b], attend over +1
+  // 1: the waves that share a KV head (heads_per_wg < 8) each stream all of its tiles for their
+  // own ceil(group / waves per head) query heads (the launch's padded group is that count);
+  // 0: they take turns on its tiles, each for the whole group.
+  int32_t qsplit;
   // Rotary embedding (with the append only): the new key is written rotated and q is rotated
   // in registers, both at position context_lens[b]; rope_cos / rope_sin [rope_rows, D/2].
   const float* rope_cos; // null: no rotation
