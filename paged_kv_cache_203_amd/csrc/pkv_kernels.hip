@@ -93,6 +93,10 @@ struct HeadSource {
   const float* rope_cos;
   const float* rope_sin;
   int rope_pos;
+  // 1: this source's tile loads keep the default cache policy instead of the non-temporal one,
+  // because another wave of the workgroup loads the same rows in the same round and should find
+  // them in L2.
+  int keep = 0;
 };
 
 template <int DT, int D, int GP, int DEPTH, bool ROPE = false>
@@ -226,11 +230,18 @@ struct HeadPipe {
     const uint32_t kdst = lds_base + uint32_t(st * Geo::KTILE);
     const gptr vb = uniform_gptr(s.vpool + base);
     const uint32_t vdst = lds_base + VSTAGE0 + uint32_t(st * Geo::KTILE);
-#pragma unroll
-    for (int i = 0; i < NKL; ++i) dma16_to_lds<kDmaPolicy>(vb + vdma_off[i], vdst + uint32_t(i * 1024));
     const gptr kb = uniform_gptr(s.kpool + base);
+    if (s.keep) {
 #pragma unroll
-    for (int i = 0; i < NKL; ++i) dma16_to_lds<kDmaPolicy>(kb + dma_off[i], kdst + uint32_t(i * 1024));
+      for (int i = 0; i < NKL; ++i) dma16_to_lds<0>(vb + vdma_off[i], vdst + uint32_t(i * 1024));
+#pragma unroll
+      for (int i = 0; i < NKL; ++i) dma16_to_lds<0>(kb + dma_off[i], kdst + uint32_t(i * 1024));
+    } else {
+#pragma unroll
+      for (int i = 0; i < NKL; ++i) dma16_to_lds<kDmaPolicy>(vb + vdma_off[i], vdst + uint32_t(i * 1024));
+#pragma unroll
+      for (int i = 0; i < NKL; ++i) dma16_to_lds<kDmaPolicy>(kb + dma_off[i], kdst + uint32_t(i * 1024));
+    }
   }
 
   // Attend to the tile held in stage `st` (its loads have completed).
@@ -871,6 +882,7 @@ __global__ __launch_bounds__(NW * 64) void step_kernel(const StepParams p) {
     src.t_end = min(a.context_lens[bb] + p.append, te * kTile);
     src.sub = qsplit ? 0 : wave / HPW;
     src.stride = qsplit ? 1 : WPH;
+    src.keep = qsplit ? 1 : 0;   // the waves that split the head's query heads load its tiles alike
     src.q_group = static_cast<const char*>(a.q) + (int64_t(bb) * a.hq + int64_t(kvh) * G + gs) * Geo::RB;
     src.rope_cos = p.rope_cos;
     src.rope_sin = p.rope_sin;
