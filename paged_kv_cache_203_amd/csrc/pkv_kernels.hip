@@ -97,6 +97,9 @@ struct HeadSource {
   // because another wave of the workgroup loads the same rows in the same round and should find
   // them in L2.
   int keep = 0;
+  // Two waves that share this head's tiles and their LDS stages: 1 loads the K rows, 2 the V
+  // rows, and both wait for each other around every tile; 0: this wave loads both.
+  int part = 0;
 };
 
 template <int DT, int D, int GP, int DEPTH, bool ROPE = false>
@@ -231,7 +234,13 @@ struct HeadPipe {
     const gptr vb = uniform_gptr(s.vpool + base);
     const uint32_t vdst = lds_base + VSTAGE0 + uint32_t(st * Geo::KTILE);
     const gptr kb = uniform_gptr(s.kpool + base);
-    if (s.keep) {
+    if (s.part == 1) {
+#pragma unroll
+      for (int i = 0; i < NKL; ++i) dma16_to_lds<kDmaPolicy>(kb + dma_off[i], kdst + uint32_t(i * 1024));
+    } else if (s.part == 2) {
+#pragma unroll
+      for (int i = 0; i < NKL; ++i) dma16_to_lds<kDmaPolicy>(vb + vdma_off[i], vdst + uint32_t(i * 1024));
+    } else if (s.keep) {
 #pragma unroll
       for (int i = 0; i < NKL; ++i) dma16_to_lds<0>(vb + vdma_off[i], vdst + uint32_t(i * 1024));
 #pragma unroll
@@ -376,6 +385,16 @@ struct HeadPipe {
       else wait_stage<N - 1>(later);
     }
   }
+  // The same for a wave that loads half of every tile (NKL loads).
+  template <int N>
+  __device__ static void wait_stage_half(int later) {
+    if constexpr (N == 0) {
+      wait_vmcnt<0>();
+    } else {
+      if (later >= N) wait_vmcnt<N * NKL>();
+      else wait_stage_half<N - 1>(later);
+    }
+  }
 
   // Stream all of this wave's tiles of `s`.  With has_next, the loads of the next run()'s q and
   // first page ids (for `next`) start as the last chunk begins (see prefetch).  When prefetch() ran for `s`,
@@ -420,11 +439,17 @@ struct HeadPipe {
       // Steady state: every stage is refilled with a tile of the chunk, so the loads issued
       // after stage d's are always those of DEPTH - 1 stages.
       for (; k + 2 * DEPTH <= nc; k += DEPTH) {
-        if (lockstep) __builtin_amdgcn_s_barrier();
+        if (lockstep && !s.part) __builtin_amdgcn_s_barrier();
 #pragma unroll
         for (int d = 0; d < DEPTH; ++d) {
-          wait_vmcnt<(DEPTH - 1) * Geo::LOADS>();
+          if (s.part) {
+            wait_vmcnt<(DEPTH - 1) * NKL>();
+            __builtin_amdgcn_s_barrier();   // the partner's half of the tile has landed too
+          } else {
+            wait_vmcnt<(DEPTH - 1) * Geo::LOADS>();
+          }
           if (ok(page_at(k + d))) process(s, d, tile_at(k + d), scale_log2, G); else bad = true;
+          if (s.part) __builtin_amdgcn_s_barrier();   // the partner is done with the stage
           issue(s, d, tile_at(k + d + DEPTH), page_at(k + d + DEPTH));
         }
       }
@@ -433,9 +458,15 @@ struct HeadPipe {
       for (; k < nc; k += DEPTH) {
 #pragma unroll
         for (int d = 0; d < DEPTH; ++d) {
-          wait_stage<DEPTH - 1>(nc - 1 - (k + d));
+          if (s.part) {
+            wait_stage_half<DEPTH - 1>(nc - 1 - (k + d));
+          } else {
+            wait_stage<DEPTH - 1>(nc - 1 - (k + d));
+          }
           if (k + d < nc) {
+            if (s.part) __builtin_amdgcn_s_barrier();
             if (ok(page_at(k + d))) process(s, d, tile_at(k + d), scale_log2, G); else bad = true;
+            if (s.part) __builtin_amdgcn_s_barrier();
           }
           if (k + d + DEPTH < nc) issue(s, d, tile_at(k + d + DEPTH), page_at(k + d + DEPTH));
         }
@@ -835,6 +866,10 @@ __global__ __launch_bounds__(NW * 64) void step_kernel(const StepParams p) {
   const int gs = qsplit ? (wave / HPW) * GW : 0;
   const int Gw = qsplit ? min(GW, G - gs) : G;
   const bool own_heads = WPH == 1 || qsplit;   // the wave alone finishes its query heads
+  // Two waves per KV head share its LDS stages: the first loads K, the second V, so that each
+  // byte a compute unit has in flight is a different one (loading every row twice halved the
+  // distinct bytes in flight and capped the stream).
+  const int part = qsplit && WPH == 2 ? (wave < HPW ? 1 : 2) : 0;
 
   __shared__ int merging[2];
   int split_first = -1, split_last = -1;   // sequences whose piece here is split
@@ -863,7 +898,7 @@ __global__ __launch_bounds__(NW * 64) void step_kernel(const StepParams p) {
   int b = sp.seq_of_tile(lo);   // the sequence holding tile `lo`
 
   HeadPipe<DT, D, GP, DEPTH, ROPE> hp;
-  hp.init(a.tok_stride, lds_addr(sm.w[wave]), &sm.p[wave][0][0], &sm.a[wave][0]);
+  hp.init(a.tok_stride, lds_addr(sm.w[part ? wave % HPW : wave]), &sm.p[wave][0][0], &sm.a[wave][0]);
 
   // This wave's source for sequence bb: the tiles of bb in this range, for its KV head.
   auto source = [&](int bb) {
@@ -882,7 +917,8 @@ __global__ __launch_bounds__(NW * 64) void step_kernel(const StepParams p) {
     src.t_end = min(a.context_lens[bb] + p.append, te * kTile);
     src.sub = qsplit ? 0 : wave / HPW;
     src.stride = qsplit ? 1 : WPH;
-    src.keep = qsplit ? 1 : 0;   // the waves that split the head's query heads load its tiles alike
+    src.keep = qsplit && !part ? 1 : 0;
+    src.part = part;   // the waves that split the head's query heads load its tiles alike
     src.q_group = static_cast<const char*>(a.q) + (int64_t(bb) * a.hq + int64_t(kvh) * G + gs) * Geo::RB;
     src.rope_cos = p.rope_cos;
     src.rope_sin = p.rope_sin;
