@@ -401,9 +401,11 @@ struct HeadPipe {
   // its q is taken here and its first page ids are used.  `at_start` runs once per call, on
   // every wave, after all of this wave's earlier memory operations have completed and before
   // any load of `s`'s tiles is issued.
-  // lockstep: every wave of the workgroup streams the same tile list (one wave per KV head); a
-  // barrier per round of DEPTH tiles then keeps the waves together, so that the rows of all
-  // heads of a token are read close in time and no wave falls behind the others.
+  // lockstep: every wave of the workgroup streams the same tile list (one wave per KV head, or
+  // waves that split a head's query heads); a barrier per round of DEPTH tiles then keeps the
+  // waves together, so that the rows of all heads of a token are read close in time and no wave
+  // falls behind the others.  Waves that share their stages (s.part) meet at a barrier around
+  // every tile instead.
   __device__ void run(const HeadSource& s, float scale_log2, int G) {
     run(s, scale_log2, G, s, false, false, [] {});
   }
@@ -652,10 +654,10 @@ __device__ inline int step_tiles(const StepParams& p, int b) {
 // refill, so it gets that much less streaming.  `wpre` is the exclusive prefix of the weights
 // (B + 1 entries, in LDS); the `groups` ranges cut the weighted line [0, WT) evenly, and a range
 // owns the tiles whose weighted start falls in it.  Everything depends on the lengths only.
-// The start weight was measured: three tiles when each wave streams a whole KV head (12 units:
-// 113.5 us for the Llama-3-8B-shaped step, against 115.5 us at 8 and 118 us at 4), six when
-// several waves take turns on one head's tiles and so each restarts on fewer of them (24 units:
-// 57.8 us for the Qwen2-7B-shaped step, against 65.5 us at 8).
+// The start weight was measured: three tiles with one wave per KV head (12 units: 113.5 us for
+// the Llama-3-8B-shaped step, against 115.5 us at 8 and 118 us at 4), six when several waves
+// share a head (24 units: 57.8 us for the Qwen2-7B-shaped step with alternating tiles, against
+// 65.5 us at 8; with the query split, 12 and 24 measure the same).
 __device__ inline int start_units(int waves_per_head) { return waves_per_head == 1 ? 12 : 24; }
 
 struct StepSplit {
