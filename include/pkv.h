@@ -90,7 +90,12 @@ typedef struct {
  * Accumulation is float32; out is rounded to the element type (round-to-nearest-even).
  * context_lens[b] <= 0 gives out[b] = 0.  Table entries past ceil(L_b / PS) and slots at or past
  * L_b in the last page are never read.  `scale` must be finite (usually 1/sqrt(D)).
- * `out` must not overlap q or the pools. */
+ * `out` must not overlap q or the pools.
+ * Follows the CacheIR page, "Compiler Example": in the decode-specialised graph, grouped-query
+ * attention over the cached keys and values becomes one paged_attention_decode(q, k, v) call per
+ * step; "Current Capabilities" names the multi-batch page-table form with the GQA head mapping.
+ * The batched form with one page table per request is the TorchInferno page's
+ * batched_paged_decode_attention ("Custom Kernels"). */
 int pkv_paged_decode_attention(const void* q, const void* k_pool, const void* v_pool,
                                const int32_t* page_table, const int32_t* context_lens,
                                float scale, void* out, const pkv_shape* shape, void* stream);
@@ -119,7 +124,11 @@ int pkv_paged_decode_attention_partial(const void* q, const void* k_pool, const 
  * With n_b = ceil(L_b / P) partitions, M = max_p lse_p and w_p = exp(lse_p - M):
  *   out[b, h, :] = sum_p w_p partial_out[b, h, p, :] / sum_p w_p   (rounded to the element type)
  *   lse_out[b, h] = M + ln sum_p w_p                               (float32; lse_out may be NULL)
- * Rows with L_b <= 0 get out = 0 and lse_out = -inf.  `out` must not overlap the partials. */
+ * Rows with L_b <= 0 get out = 0 and lse_out = -inf.  `out` must not overlap the partials.
+ * This is the reduce half of the CacheIR page's reduced (split, then reduced) paged-attention
+ * decode ("Current Capabilities", native backend row); the pages give no formula for the
+ * reduction, and the one above is the exact combination of softmax partials by their
+ * log-sum-exps. */
 int pkv_lse_merge(const float* partial_out, const float* partial_lse,
                   const int32_t* context_lens, int32_t partition_tokens, int32_t max_partitions,
                   void* out, float* lse_out, const pkv_shape* shape, void* stream);
@@ -277,7 +286,12 @@ size_t pkv_decode_step_workspace_bytes(const pkv_shape* shape);
  *   bit 0 (1): a live table entry outside [0, num_pages)
  *   bit 1 (2): n > max_pages_per_seq (the length exceeds the table's capacity)
  *   bit 2 (4): with check_append_unique != 0, a row's append page (entry context_lens[b] / PS)
- *              is also a live entry of another row. */
+ *              is also a live entry of another row.
+ * The host-side checks of every call cover what the host can see; this call covers the
+ * device-resident metadata.  It follows the CacheIR page, "Boundaries" (paged KV-cache reference
+ * behaviour and shared page allocator accounting among the implemented, tested boundaries) and
+ * the Infinity docs, "Current execution limits", where every boundary and retained length is
+ * checked before GPU work and destination rows must be unique and in range. */
 int pkv_validate_metadata(const int32_t* page_table, const int32_t* context_lens,
                           int32_t extra_tokens, int32_t check_append_unique,
                           int32_t* device_status, const pkv_shape* shape, void* stream);
