@@ -12,11 +12,17 @@ made by one call of pkv_paged_decode_step (one kernel launch):
 Inputs are seeded synthetic data, resident in HBM before timing starts.  The pools rotate over
 several replicas so that no step finds the previous step's KV in the 256 MB Infinity Cache.
 
+Timing: W untimed steps, then the timed region, K steps launched back to back between two HIP
+events on the launch stream (their average is the step kernel's average launch duration, and the
+host clock around the same region gives the step rate), then K more steps each bracketed by its
+own event pair for the median / p10 / p90 (an event pair per launch adds a few us to each).
+
 Prints one JSON line: whole-step throughput in algorithmic GB/s (KV rows of every live token once,
 q, out, page-table entries and the append rows), decode tokens/s (= sequences per step / step
-time), the roofline of the dominant kernel measured with HIP events on the launch stream (and the
-HBM traffic that rocprofv3 counters measured for it, when those were taken on the current kernel
-source), and the fp64 CPU oracle's rate on the host for reference.
+time), the roofline of the dominant kernel (and the HBM traffic that rocprofv3 counters measured
+for it, when those were taken on the current kernel source), a plain copy's and a plain read
+stream's rate on the same device, every workload of the suite on its own paths (`configs`), and
+the fp64 CPU oracle's rate on the host for reference.
 """
 from __future__ import annotations
 
@@ -61,6 +67,10 @@ def parse():
                     help="minimum host time spent timing the CPU oracle (0 disables it)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of known size (counter calibration)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-workload sweep (every workload of the suite, its own paths)")
+    ap.add_argument("--config-steps", type=int, default=50, help="timed calls per path in the sweep")
+    ap.add_argument("--config-warmup", type=int, default=5)
     return ap.parse_args()
 
 
@@ -143,6 +153,8 @@ def measured_traffic(workload):
 
 
 def copy_calibration(nbytes=2 << 30, reps=20):
+    """A plain device copy of `nbytes` into another buffer (torch's copy kernel): the read + write
+    rate, and the kernel the counter calibration reads."""
     import torch
     a = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").normal_()
     b = torch.empty_like(a)
@@ -158,45 +170,313 @@ def copy_calibration(nbytes=2 << 30, reps=20):
     ms = s.elapsed_time(e) / reps
     gbs = 2 * nbytes / (ms * 1e-3) / 1e9
     log(f"plain copy: {nbytes / 2**30:.1f} GiB read + write, {ms:.3f} ms/launch, {gbs:.0f} GB/s")
-    return {"bytes_read": nbytes, "bytes_written": nbytes, "ms": ms, "gbs": gbs}
+    del a, b
+    return {"bytes_read": nbytes, "bytes_written": nbytes, "ms": round(ms, 5), "gbs": round(gbs, 1)}
+
+
+def read_calibration(pkv, nbytes=4 << 30, reps=20):
+    """The library's plain read stream over `nbytes` (each byte read once per launch): the read
+    bandwidth this device reaches, the practical ceiling beside the 8 TB/s peak."""
+    import torch
+    buf = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda").random_()
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        pkv.read_stream(buf, sink)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        pkv.read_stream(buf, sink)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / reps
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log(f"plain read stream: {nbytes / 2**30:.1f} GiB, {ms:.3f} ms/launch, {gbs:.0f} GB/s")
+    del buf
+    return {"bytes_read": nbytes, "ms": round(ms, 5), "gbs": round(gbs, 1)}
+
+
+def cpu_info():
+    model = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        affinity = os.cpu_count()
+    return {"cpu": model, "affinity_cores": affinity, "os_cpu_count": os.cpu_count()}
+
+
+def cpu_threads():
+    """Host threads for the oracle: the affinity cores, capped at 16 (the GPU machine's CPU share)."""
+    return max(1, min(16, cpu_info()["affinity_cores"]))
+
+
+def run_oracle_rows(w, pools, threads):
+    """The fp64 oracle over all rows of `w` against `pools`, rows spread over `threads` host
+    threads (NumPy releases the interpreter lock inside its array operations); BLAS is limited to
+    one thread per call, so `threads` is the core count the oracle uses."""
+    import numpy as np
+    import oracle as O
+    import workloads as W
+    from concurrent.futures import ThreadPoolExecutor
+    B = w.cfg.batch
+    chunks = [list(range(B))[i::threads] for i in range(min(threads, B))]
+
+    def part(rows):
+        sub = W.subset_rows(w, rows)
+        O.paged_decode_attention(sub.q, pools[0], pools[1], sub.page_table, sub.context_lens,
+                                 sub.scale, sub.dtype)
+
+    with ThreadPoolExecutor(len(chunks)) as ex:
+        list(ex.map(part, chunks))
+
+
+def blas_limits():
+    try:
+        from threadpoolctl import threadpool_limits
+        return threadpool_limits(limits=1)
+    except ImportError:  # pragma: no cover
+        import contextlib
+        return contextlib.nullcontext()
 
 
 def cpu_baseline(w, extra_new, seconds):
-    """Time the fp64 oracle (append + attention) on the host over a bounded sample."""
+    """Time the fp64 oracle (append + attention) on the host over a bounded sample: whole steps
+    of the workload, repeated until `seconds` have passed."""
     import numpy as np
     import oracle as O
-    try:
-        from threadpoolctl import threadpool_limits
-    except ImportError:  # pragma: no cover
-        threadpool_limits = None
-    rows = list(range(w.cfg.batch))
     k_new, v_new, append_lens = extra_new
-
-    def one():
-        kp, vp = O.paged_kv_append(w.k_pool, w.v_pool, k_new, v_new, w.page_table, append_lens)
-        O.paged_decode_attention(w.q, kp, vp, w.page_table, w.context_lens, w.scale, w.dtype)
-
-    ctx = threadpool_limits(limits=1) if threadpool_limits else None
-    if ctx:
-        ctx.__enter__()
-    try:
+    threads = cpu_threads()
+    with blas_limits():
         n = 0
         t0 = time.perf_counter()
         while True:
-            one()
+            kp, vp = O.paged_kv_append(w.k_pool, w.v_pool, k_new, v_new, w.page_table, append_lens)
+            run_oracle_rows(w, (kp, vp), threads)
             n += 1
             if time.perf_counter() - t0 >= seconds:
                 break
         dt = (time.perf_counter() - t0) / n
-    finally:
-        if ctx:
-            ctx.__exit__(None, None, None)
     kv = int(np.maximum(w.context_lens.astype(np.int64), 0).sum()) * w.kv_bytes_per_token()
-    return {"value": round(kv / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "tokens_per_s": round(len(rows) / dt, 3), "s_per_step": round(dt, 4),
-            "sample": (f"whole {w.cfg.name} step (append + attention, all {len(rows)} rows), "
-                       f"{n} repetition(s), float64 NumPy, BLAS limited to 1 thread"),
-            "cpu": platform.processor() or platform.machine()}
+    info = cpu_info()
+    return {"value": round(kv / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "tokens_per_s": round(w.cfg.batch / dt, 3), "s_per_step": round(dt, 4),
+            "sample": (f"{n} whole {w.cfg.name} step(s) (append + attention, all "
+                       f"{w.cfg.batch} rows), float64 NumPy, rows over {threads} host threads, "
+                       f"BLAS 1 thread per call"),
+            "blas_threads_per_call": 1, **info}
+
+
+def timed(fn, K, W, stream):
+    """Run fn(i) W times untimed, then K times back to back between two events on `stream`
+    (the timed region), then K more times with an event pair around each call (the spread).
+    Returns the per-call averages of the region (events and host wall clock) and the median,
+    p10 and p90 of the individually bracketed calls."""
+    import numpy as np
+    import torch
+    for i in range(W):
+        fn(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(K):
+        fn(W + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    region_ms = e0.elapsed_time(e1) / K
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    for i in range(K):
+        evs[i][0].record(stream)
+        fn(W + K + i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    per = np.array([a.elapsed_time(b) for a, b in evs])
+    return {"wall_us": wall * 1e6 / K, "region_us": region_ms * 1e3,
+            "median_us": float(np.median(per)) * 1e3, "p10_us": float(np.percentile(per, 10)) * 1e3,
+            "p90_us": float(np.percentile(per, 90)) * 1e3, "mean_bracketed_us": float(per.mean()) * 1e3}
+
+
+def to_device(arr, dtype, device):
+    import numpy as np
+    import torch
+    a = np.ascontiguousarray(arr)
+    if dtype == "bf16":
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(a).to(device)
+
+
+class Prepared:
+    """One workload on the device: q, table, lengths, the new rows, and `R` replicas of the pools
+    (rotated per call so that the 256 MB Infinity Cache never holds the next call's KV)."""
+
+    def __init__(self, w, replicas, dev):
+        import numpy as np
+        import torch
+        from workloads.generate import STREAM_KNEW, STREAM_VNEW, fill_normal
+        cfg = w.cfg
+        self.w, self.cfg = w, cfg
+        B, Hkv, D = cfg.batch, cfg.num_kv_heads, cfg.head_dim
+        if cfg.append:
+            k_new, v_new, append_lens = w.k_new, w.v_new, w.append_lens
+        else:
+            # The step writes its own token: the new row lands at position L - 1, so that
+            # attention covers exactly the workload's context lengths.
+            k_new = fill_normal((B, Hkv, D), cfg.dtype, w.seed, STREAM_KNEW)
+            v_new = fill_normal((B, Hkv, D), cfg.dtype, w.seed, STREAM_VNEW)
+            append_lens = (w.context_lens - 1).astype(np.int32)
+        self.new_rows = (k_new, v_new, append_lens)
+        self.q = to_device(w.q, cfg.dtype, dev)
+        self.table = torch.from_numpy(w.page_table).to(dev)
+        self.lens = torch.from_numpy(w.context_lens).to(dev)
+        self.alens = torch.from_numpy(append_lens).to(dev)
+        self.kn = to_device(k_new, cfg.dtype, dev)
+        self.vn = to_device(v_new, cfg.dtype, dev)
+        k0 = to_device(w.k_pool, cfg.dtype, dev)
+        v0 = to_device(w.v_pool, cfg.dtype, dev)
+        self.pool_bytes = 2 * k0.numel() * k0.element_size()
+        self.R = replicas or min(64, max(1, math.ceil((2 << 30) / self.pool_bytes)))
+        self.pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(self.R - 1)]
+        self.out = torch.empty_like(self.q)
+        self.scale = float(w.scale)
+
+    def release(self):
+        self.pools = None
+
+
+def config_sweep(pkv, dev, stream, read_gbs, K, W, cpu_seconds):
+    """Every workload of the suite on its own paths: median / p10 / p90 per call, algorithmic
+    GB/s, % of 8 TB/s and of this run's read-stream ceiling, decode tokens/s; pools rotated (and,
+    where the KV fits in the Infinity Cache, also the same buffers every call); the fp64 oracle
+    timed once per workload on the host."""
+    import numpy as np
+    import torch
+    import oracle as O
+    import workloads as W_
+    res = {}
+    for idx in (1, 2, 3, 4, 5):
+        t_gen = time.perf_counter()
+        cfg = W_.config(idx)
+        w = W_.make_workload(cfg)
+        log(f"[configs] {cfg.name}: generated in {time.perf_counter() - t_gen:.1f}s")
+        pr = Prepared(w, None, dev)
+        ws = torch.zeros(pkv.decode_step_workspace_bytes(pr.q, pr.pools[0][0], pr.table),
+                         dtype=torch.uint8, device=dev)
+        B = cfg.batch
+        entry = {"description": cfg.description, "batch": B, "live_tokens": w.logical_tokens(),
+                 "pool_replicas": pr.R, "paths": {}}
+        PS = cfg.page_size
+        P = cfg.partition_tokens or 512
+
+        def rec(name, fn, nbytes, same_buffer=False, extra=None):
+            r = timed(fn, K, W, stream)
+            d = {"bytes": nbytes, "avg_us": round(r["region_us"], 3), "wall_us": round(r["wall_us"], 3),
+                 "median_us": round(r["median_us"], 3), "p10_us": round(r["p10_us"], 3),
+                 "p90_us": round(r["p90_us"], 3)}
+            gbs = nbytes / (r["region_us"] * 1e-6) / 1e9
+            d.update(gbs=round(gbs, 1), pct_of_hbm_peak=round(100 * gbs / HBM_PEAK_GBS, 2),
+                     pct_of_read_stream=round(100 * gbs / read_gbs, 2) if read_gbs else None,
+                     decode_tokens_per_s=round(B / (r["region_us"] * 1e-6), 1))
+            if extra:
+                d.update(extra)
+            if same_buffer:
+                r2 = timed(lambda i: fn(0), K, W, stream)
+                d["same_buffer_avg_us"] = round(r2["region_us"], 3)
+                d["same_buffer_gbs"] = round(nbytes / (r2["region_us"] * 1e-6) / 1e9, 1)
+            entry["paths"][name] = d
+            log(f"[configs] {cfg.name} {name}: {d['avg_us']:.1f} us/call, {d['gbs']:.0f} GB/s "
+                f"({d['pct_of_hbm_peak']:.1f}% of 8 TB/s)"
+                + (f", same buffers {d['same_buffer_avg_us']:.1f} us" if same_buffer else ""))
+
+        kn, vn = pr.kn, pr.vn
+        fits_cache = pr.pool_bytes < (1 << 30)
+
+        def step(i):
+            kp, vp = pr.pools[i % pr.R]
+            pkv.paged_decode_step(pr.q, kp, vp, pr.table, pr.alens, pr.scale, k_new=kn, v_new=vn,
+                                  out=pr.out, workspace=ws)
+
+        nb = step_bytes(w, P, "step")
+        extra = {}
+        if cfg.lengths[0] == "prefix":
+            uniq = w.unique_tokens() * w.kv_bytes_per_token()
+            extra = {"effective_gbs_logical_bytes": None, "unique_kv_bytes": uniq}
+        rec("step", step, nb["step"], same_buffer=fits_cache, extra=extra)
+        if cfg.lengths[0] == "prefix":
+            d = entry["paths"]["step"]
+            d["effective_gbs_logical_bytes"] = d["gbs"]
+            # headline for the shared-prefix batch: the unique physical bytes
+            ub = nb["step"] - nb["kv"] + uniq
+            d["unique_bytes"] = ub
+            d["gbs"] = round(ub / (d["avg_us"] * 1e-6) / 1e9, 1)
+            d["pct_of_hbm_peak"] = round(100 * d["gbs"] / HBM_PEAK_GBS, 2)
+            # the shared-prefix (cascade) decode over the same batch
+            Pc = 256
+            maxp = pkv.partitions_needed(PS, w.page_table.shape[1], Pc)
+            po = torch.empty((B, cfg.num_q_heads, maxp, cfg.head_dim), dtype=torch.float32, device=dev)
+            pl = torch.empty((B, cfg.num_q_heads, maxp), dtype=torch.float32, device=dev)
+            prefix_tokens = w.shared_pages * PS
+            prefix_pages = torch.from_numpy(np.ascontiguousarray(w.page_table[0, :w.shared_pages])).to(dev)
+
+            def cascade(i):
+                kp, vp = pr.pools[i % pr.R]
+                pkv.paged_decode_cascade(pr.q, kp, vp, prefix_pages, prefix_tokens, pr.table, pr.lens,
+                                         Pc, pr.scale, out=pr.out, partial_out=po, partial_lse=pl)
+
+            rec("cascade", cascade, step_bytes(w, Pc, "cascade")["kernel"], same_buffer=fits_cache,
+                extra={"partition_tokens": Pc, "note": "without the append (attention only)"})
+        if cfg.append:
+            def separate(i):
+                kp, vp = pr.pools[i % pr.R]
+                pkv.paged_kv_append(kn, vn, kp, vp, pr.table, pr.alens)
+                pkv.paged_decode_attention(pr.q, kp, vp, pr.table, pr.lens, pr.scale, pr.out)
+            rec("append_then_single_pass", separate, nb["step"], same_buffer=fits_cache,
+                extra={"note": "two launches: pkv_paged_kv_append, then pkv_paged_decode_attention"})
+        if cfg.partition_tokens:
+            maxp = pkv.partitions_needed(PS, w.page_table.shape[1], P)
+            po = torch.empty((B, cfg.num_q_heads, maxp, cfg.head_dim), dtype=torch.float32, device=dev)
+            pl = torch.empty((B, cfg.num_q_heads, maxp), dtype=torch.float32, device=dev)
+
+            def split(i):
+                kp, vp = pr.pools[i % pr.R]
+                pkv.paged_decode_attention_partial(pr.q, kp, vp, pr.table, pr.lens, P, pr.scale, po, pl, maxp)
+                pkv.lse_merge(po, pl, pr.lens, P, PS, w.page_table.shape[1], out=pr.out)
+
+            append_bytes = 2 * (2 * B * cfg.num_kv_heads * cfg.head_dim * cfg.elem_bytes)
+            rec("split_kv_and_merge", split, step_bytes(w, P, "split")["step"] - append_bytes,
+                extra={"partition_tokens": P, "note": "attention only: partial launch + merge launch"})
+        pr.release()
+        del ws
+        torch.cuda.empty_cache()
+        # the oracle, once per workload (best of three for the tiny one)
+        if cpu_seconds > 0:
+            threads = cpu_threads()
+            k_new, v_new, append_lens = pr.new_rows
+            best = None
+            with blas_limits():
+                for _ in range(3 if idx == 1 else 1):
+                    t0 = time.perf_counter()
+                    kp, vp = O.paged_kv_append(w.k_pool, w.v_pool, k_new, v_new, w.page_table, append_lens)
+                    run_oracle_rows(w, (kp, vp), threads)
+                    dt = time.perf_counter() - t0
+                    best = dt if best is None else min(best, dt)
+            kvb = w.logical_tokens() * w.kv_bytes_per_token()
+            entry["oracle"] = {"s_per_step": round(best, 4), "tokens_per_s": round(B / best, 2),
+                               "logical_kv_gbs": round(kvb / best / 1e9, 4), "cores": threads,
+                               "runs": 3 if idx == 1 else 1}
+            log(f"[configs] {cfg.name} oracle: {best:.3f} s/step on {threads} threads")
+        res[cfg.name] = entry
+        del w, pr
+    return res
 
 
 def main():
@@ -212,7 +492,6 @@ def main():
 
     import paged_kv_cache_203_amd as pkv
     import workloads as W
-    from workloads.generate import STREAM_KNEW, STREAM_VNEW, fill_normal
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
@@ -224,14 +503,6 @@ def main():
     t_gen = time.perf_counter()
     w = W.make_workload(cfg)
     B, Hq, Hkv, D, PS = cfg.batch, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.page_size
-    if cfg.append:
-        k_new, v_new, append_lens = w.k_new, w.v_new, w.append_lens
-    else:
-        # The decode step writes its own token: the new row lands at position L - 1, so that
-        # attention covers exactly the workload's context lengths.
-        k_new = fill_normal((B, Hkv, D), cfg.dtype, w.seed, STREAM_KNEW)
-        v_new = fill_normal((B, Hkv, D), cfg.dtype, w.seed, STREAM_VNEW)
-        append_lens = (w.context_lens - 1).astype(np.int32)
     w.q_tokens = args.q_tokens if args.path == "multiquery" else 1
     if args.path == "cascade" and cfg.lengths[0] != "prefix":
         raise SystemExit("--path cascade needs a prefix-shared workload")
@@ -240,25 +511,11 @@ def main():
     log(f"workload {cfg.name}: generated in {time.perf_counter() - t_gen:.1f}s, "
         f"{w.logical_tokens()} live tokens, pool {w.k_pool.shape}")
 
-    def to_device(arr, dtype, device):
-        a = np.ascontiguousarray(arr)
-        if dtype == "bf16":
-            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
-        return torch.from_numpy(a).to(device)
-
+    from workloads.generate import fill_normal
     dev = torch.device("cuda:0")
-    q = to_device(w.q, cfg.dtype, dev)
-    table = torch.from_numpy(w.page_table).to(dev)
-    lens = torch.from_numpy(w.context_lens).to(dev)
-    alens = torch.from_numpy(append_lens).to(dev)
-    kn = to_device(k_new, cfg.dtype, dev)
-    vn = to_device(v_new, cfg.dtype, dev)
-    k0 = to_device(w.k_pool, cfg.dtype, dev)
-    v0 = to_device(w.v_pool, cfg.dtype, dev)
-    pool_bytes = 2 * k0.numel() * k0.element_size()
-    R = args.replicas or max(1, math.ceil((2 << 30) / pool_bytes))
-    pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(R - 1)]
-    out = torch.empty_like(q)
+    pr = Prepared(w, args.replicas, dev)
+    q, table, lens, alens, kn, vn, out = pr.q, pr.table, pr.lens, pr.alens, pr.kn, pr.vn, pr.out
+    pools, R = pr.pools, pr.R
     maxp = pkv.partitions_needed(PS, w.page_table.shape[1], P)
     if args.path == "multiquery":
         T = args.q_tokens
@@ -268,7 +525,7 @@ def main():
         plm = torch.empty((B, T, Hq, maxp), dtype=torch.float32, device=dev)
     po = torch.empty((B, Hq, maxp, D), dtype=torch.float32, device=dev)
     pl = torch.empty((B, Hq, maxp), dtype=torch.float32, device=dev)
-    scale = float(w.scale)
+    scale = pr.scale
     stream = torch.cuda.current_stream(dev)
 
     prefix_tokens = w.shared_pages * PS
@@ -282,17 +539,14 @@ def main():
         rope = dict(rope_cos=torch.from_numpy(rc).to(dev), rope_sin=torch.from_numpy(rs).to(dev))
     ws = None
     if args.path == "step":
-        ws = torch.zeros(pkv.decode_step_workspace_bytes(q, k0, table), dtype=torch.uint8, device=dev)
+        ws = torch.zeros(pkv.decode_step_workspace_bytes(q, pools[0][0], table), dtype=torch.uint8, device=dev)
 
     def step(i, ev=None):
+        """One step; with `ev`, the event pair brackets the dominant kernel only."""
         kp, vp = pools[i % R]
         if args.path == "step":
-            if ev is not None:
-                ev[0].record(stream)
             pkv.paged_decode_step(q, kp, vp, table, alens, scale, k_new=kn, v_new=vn, out=out,
                                   workspace=ws, **rope)
-            if ev is not None:
-                ev[1].record(stream)
             return
         if args.path != "multiquery":   # the multi-query rows' K/V are already in the pages
             pkv.paged_kv_append(kn, vn, kp, vp, table, alens)
@@ -318,41 +572,70 @@ def main():
             if ev is not None:
                 ev[1].record(stream)
 
+    # ---- the timed region: K steps back to back between two events on the launch stream ----
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-
     K = args.steps
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(K)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    e0.record(stream)
     for i in range(K):
-        step(args.warmup + i, evs[i])
+        step(args.warmup + i)
+    e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kernel_ms = [a.elapsed_time(b) for a, b in evs]
+    region_us = e0.elapsed_time(e1) * 1e3 / K
+
+    # ---- the spread: K more steps, each bracketed by its own event pair ----
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    for i in range(K):
+        if args.path == "step":
+            evs[i][0].record(stream)
+            step(args.warmup + K + i)
+            evs[i][1].record(stream)
+        else:
+            step(args.warmup + K + i, evs[i])
+    torch.cuda.synchronize()
+    kernel_us = np.array([a.elapsed_time(b) for a, b in evs]) * 1e3
 
     nb = step_bytes(w, P, args.path)
     ms_step = wall * 1e3 / K
     gbs = nb["step"] / (ms_step * 1e-3) / 1e9
-    k_avg = float(np.mean(kernel_ms))
-    k_gbs = nb["kernel"] / (k_avg * 1e-3) / 1e9
-    log(f"{K} steps in {wall * 1e3:.2f} ms: {ms_step * 1e3:.1f} us/step, {gbs:.0f} GB/s step, "
-        f"dominant kernel {k_avg * 1e3:.1f} us avg (p10 {np.percentile(kernel_ms, 10) * 1e3:.1f}, "
-        f"p90 {np.percentile(kernel_ms, 90) * 1e3:.1f}), {k_gbs:.0f} GB/s")
+    # One launch per step on the step path: the region's average is the kernel's average launch
+    # duration in a back-to-back stream.  Other paths time their dominant kernel alone.
+    k_avg_us = region_us if args.path == "step" else float(kernel_us.mean())
+    k_gbs = nb["kernel"] / (k_avg_us * 1e-6) / 1e9
+    log(f"{K} steps in {wall * 1e3:.2f} ms: {ms_step * 1e3:.1f} us/step, {gbs:.0f} GB/s step; "
+        f"events over the region {region_us:.1f} us/step; dominant kernel {k_avg_us:.1f} us avg, "
+        f"{k_gbs:.0f} GB/s; individually bracketed: median {np.median(kernel_us):.1f}, "
+        f"p10 {np.percentile(kernel_us, 10):.1f}, p90 {np.percentile(kernel_us, 90):.1f} us")
+
+    calib = {}
+    configs = None
+    if args.path == "step" and not args.rope and args.config == 2 and not args.no_configs:
+        calib["copy"] = copy_calibration()
+        calib["read_stream"] = read_calibration(pkv)
+        pr.release()
+        pools = None
+        torch.cuda.empty_cache()
+        configs = config_sweep(pkv, dev, stream, calib["read_stream"]["gbs"], args.config_steps,
+                               args.config_warmup, args.cpu_seconds)
 
     cpu = None
     if args.cpu_seconds > 0:
         log(f"timing the CPU oracle for >= {args.cpu_seconds:.0f}s ...")
-        cpu = cpu_baseline(w, (k_new, v_new, append_lens), args.cpu_seconds)
-        log(f"CPU oracle: {cpu['s_per_step']:.3f} s/step, {cpu['value']} GB/s")
+        cpu = cpu_baseline(w, pr.new_rows, args.cpu_seconds)
+        log(f"CPU oracle: {cpu['s_per_step']:.3f} s/step, {cpu['value']} GB/s on {cpu['cores']} threads")
 
     kernel_name = {"split": "decode_kernel (split-KV partial attention)",
                    "cascade": "pkv_paged_decode_cascade (prefix on MFMA + suffix partitions + merge)",
                    "multiquery": "pkv_paged_decode_multi_query (partitions on MFMA + merge)",
                    "single": "decode_kernel (single pass)",
                    "step": "step_kernel (pkv_paged_decode_step: append + balanced attention + merge)"}[args.path]
+    traffic = measured_traffic(cfg.name) if args.path == "step" and not args.rope else None
     line = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -391,15 +674,24 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(k_gbs / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(cfg.name) if args.path == "step" else None,
+            "traffic": traffic,
+            "traffic_source": (f"profiles/{os.path.basename(TRAFFIC_SUMMARY)}: rocprofv3 FETCH_SIZE and "
+                               "WRITE_SIZE per dispatch, scaled by a plain copy's, taken on kernel "
+                               f"sources {kernel_source_hash()} (the current ones)") if traffic else None,
             "bytes_per_launch": nb["kernel"],
-            "avg_launch_us": round(k_avg * 1e3, 3),
-            "median_launch_us": round(float(np.median(kernel_ms)) * 1e3, 3),
-            "p10_launch_us": round(float(np.percentile(kernel_ms, 10)) * 1e3, 3),
-            "p90_launch_us": round(float(np.percentile(kernel_ms, 90)) * 1e3, 3),
+            "avg_launch_us": round(k_avg_us, 3),
+            "timing": ("events on the launch stream around the K back-to-back steps of the timed "
+                       "region, divided by K" if args.path == "step" else
+                       "an event pair around the dominant kernel of each step, averaged"),
+            "median_bracketed_us": round(float(np.median(kernel_us)), 3),
+            "p10_bracketed_us": round(float(np.percentile(kernel_us, 10)), 3),
+            "p90_bracketed_us": round(float(np.percentile(kernel_us, 90)), 3),
+            "pct_of_read_stream": round(100 * k_gbs / calib["read_stream"]["gbs"], 2) if calib else None,
             "kernel_source_sha256": kernel_source_hash(),
         },
         "cpu_baseline": cpu,
+        "calibration": calib or None,
+        "configs": configs,
         "device": torch.cuda.get_device_name(0),
         "gfx_arch": getattr(torch.cuda.get_device_properties(0), "gcnArchName", None),
         "hip": getattr(torch.version, "hip", None),

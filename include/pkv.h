@@ -252,11 +252,15 @@ int pkv_rope_kv_append(const void* q, const void* k_new, const void* v_new, void
  *
  * workspace: caller-owned device memory of at least pkv_decode_step_workspace_bytes(shape)
  * bytes (queried on the same device), 16-byte aligned, zero-filled before its first use.  The
- * counters sit at its start, sized for the largest batch, and every call leaves them at zero, so
- * one workspace serves later calls without clearing as long as num_kv_heads stays the same (any
- * batch up to the one it was sized for); zero it again before using it for another head count.
- * Calls that share a workspace must not run concurrently.  Supports batch <= 4096 and
- * num_q_heads <= 1024 (else PKV_EUNSUPPORTED). */
+ * counters sit at its start, sized for the largest batch.  Each is tagged with the generation of
+ * the call that last counted into it (every call of the step in a process takes a new, larger
+ * generation on the host), so a count that an unfinished earlier call left behind is discarded
+ * by the next call rather than merged; every completed call also leaves its counters at zero.
+ * One workspace therefore serves later calls without clearing as long as num_kv_heads stays the
+ * same (any batch up to the one it was sized for); zero it again before using it for another
+ * head count.  A call captured in a graph keeps its generation for every replay, which the zeros
+ * a completed replay leaves make safe.  Calls that share a workspace must not run concurrently.
+ * Supports batch <= 4096 and num_q_heads <= 1024 (else PKV_EUNSUPPORTED). */
 int pkv_paged_decode_step(const void* q, const void* k_new, const void* v_new, void* k_pool,
                           void* v_pool, const int32_t* page_table, const int32_t* context_lens,
                           float scale, void* workspace, size_t workspace_bytes, void* out,
@@ -357,6 +361,15 @@ const char* pkv_pages_last_error(void);
 
 /* Bytes of partial_out plus partial_lse for `max_partitions` partitions (0 on a bad shape). */
 size_t pkv_partial_workspace_bytes(const pkv_shape* shape, int32_t max_partitions);
+
+/* Plain read stream, for measurement: every byte of src[0, bytes) is read once with 16-byte
+ * loads spread over the whole device, and the words read are folded by XOR into *sink (a device
+ * uint32, not cleared here).  Its rate is the read bandwidth this device actually reaches, the
+ * ceiling the decode calls' algorithmic bytes per second are reported against beside the
+ * published HBM peak (the CacheIR page, "Latest local validation", reports a bandwidth
+ * calibration beside its kernel timings).  src and bytes must be multiples of 16
+ * (PKV_EINVAL otherwise). */
+int pkv_read_stream(const void* src, size_t bytes, uint32_t* sink, void* stream);
 
 /* Message describing the calling thread's last non-zero return ("" if none). */
 const char* pkv_last_error(void);

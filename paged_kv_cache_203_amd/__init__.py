@@ -11,5 +11,5 @@ from ._lib import (LIB_PATH, PkvError, PkvShape, STATUS_APPEND_ALIAS, STATUS_CAP
                    paged_decode_step,
                    decode_step_workspace_bytes,
                    paged_decode_attention_split, paged_kv_append, partial_workspace_bytes,
-                   rope_kv_append, copy_pages, PageAllocator,
+                   rope_kv_append, copy_pages, PageAllocator, read_stream,
                    partitions_needed, validate_metadata, version)

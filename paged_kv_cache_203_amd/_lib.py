@@ -66,6 +66,7 @@ _SIGNATURES = {
                                                     _i32, _vp, _vp, _i32, _vp, _vp,
                                                     ctypes.POINTER(PkvShape), _vp]),
     "pkv_copy_pages": (ctypes.c_int, [_vp, _vp, _vp, _i32, ctypes.POINTER(PkvShape), _vp]),
+    "pkv_read_stream": (ctypes.c_int, [_vp, ctypes.c_size_t, _vp, _vp]),
     "pkv_pages_create": (_vp, [_i32, _i32]),
     "pkv_pages_destroy": (None, [_vp]),
     "pkv_pages_free_count": (_i32, [_vp]),
@@ -498,6 +499,17 @@ def copy_pages(k_pool, v_pool, pairs) -> None:
     s = make_shape(0, Hkv, Hkv, D, PS, NP, 1, _dtype_code(k_pool))
     _check(lib.pkv_copy_pages(k_pool.data_ptr(), v_pool.data_ptr(), pairs.data_ptr(),
                               int(pairs.shape[0]), ctypes.byref(s), _stream(k_pool.device)))
+
+
+def read_stream(buf, sink) -> None:
+    """Read every byte of the contiguous device tensor ``buf`` once (measurement of the device's
+    read bandwidth); the words read are folded by XOR into ``sink`` (a device int32 tensor of one
+    element or more, first element used)."""
+    torch = _torch()
+    _require(buf, "buf")
+    _require(sink, "sink", dtype=torch.int32, device=buf.device)
+    _check(lib.pkv_read_stream(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(),
+                               _stream(buf.device)))
 
 
 def _page_check(rc: int) -> None:

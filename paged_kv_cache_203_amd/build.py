@@ -30,7 +30,7 @@ HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
              "-I", os.path.join(ROOT, "include")]
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", os.path.join(ROOT, "include")]
 
-HIP_SOURCES = ["pkv_kernels.hip", "pkv_prefix.hip", "pkv_rope.hip", "pkv_api.hip"]
+HIP_SOURCES = ["pkv_kernels.hip", "pkv_prefix.hip", "pkv_rope.hip", "pkv_stream.hip", "pkv_api.hip"]
 HOST_SOURCES = ["pkv_check.cpp", "pkv_pages.cpp"]
 
 

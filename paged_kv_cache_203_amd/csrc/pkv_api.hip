@@ -1,17 +1,32 @@
 // C-ABI entry points of libpkv (declared in include/pkv.h): host-side checks, then one launch on
-// the caller's stream.  No allocation, no synchronisation, no state kept between calls.
+// the caller's stream.  No allocation and no synchronisation; the only state kept between calls
+// is the decode step's call generation (one counter per process).
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <string>
 
 #include "../../include/pkv.h"
+#include "pkv_arrival.h"
 #include "pkv_check.h"
 #include "pkv_launch.h"
 
 namespace {
 
 thread_local std::string g_last_error;
+
+// Generation of the decode step's calls in this process (pkv_arrival.h): every call takes the
+// next one, so a counter that an earlier call left behind counts from zero again.
+std::atomic<uint32_t> g_step_generation{0};
+
+uint32_t take_generation() {
+  uint32_t g = g_step_generation.load(std::memory_order_relaxed), n;
+  do {
+    n = pkv::next_generation(g);
+  } while (!g_step_generation.compare_exchange_weak(g, n, std::memory_order_relaxed));
+  return n;
+}
 
 int set_error(int code, const std::string& msg) {
   g_last_error = msg;
@@ -293,7 +308,8 @@ int decode_step(const char* name, const void* q, const void* k_new, const void* 
   char* w = static_cast<char*>(workspace);
   p.ws_out = reinterpret_cast<float*>(w + ws.out_off);
   p.ws_lse = reinterpret_cast<float*>(w + ws.lse_off);
-  p.ws_count = reinterpret_cast<int32_t*>(w + ws.count_off);
+  p.ws_count = reinterpret_cast<uint64_t*>(w + ws.count_off);
+  p.generation = take_generation();
   p.out = out;
   p.lse_out = lse_out;
   p.groups = int32_t(groups);
@@ -438,6 +454,21 @@ int pkv_copy_pages(void* k_pool, void* v_pool, const int32_t* pairs, int32_t n_p
                  pkv::elem_bytes(shape->dtype);
   (void)hipGetLastError();
   return launch_status(pkv::launch_copy_pages(p, static_cast<hipStream_t>(stream)), "pkv_copy_pages");
+}
+
+int pkv_read_stream(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+  if (!src || !sink) return set_error(PKV_EINVAL, "pkv_read_stream: src and sink must be non-NULL");
+  if (reinterpret_cast<uintptr_t>(src) % 16 != 0 || bytes % 16 != 0)
+    return set_error(PKV_EINVAL, "pkv_read_stream: src and bytes must be multiples of 16");
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return set_error(PKV_ELAUNCH, "pkv_read_stream: no device");
+  (void)hipGetLastError();
+  // Four 8-wave workgroups per compute unit: every SIMD keeps eight waves of loads in flight.
+  return launch_status(pkv::launch_read_stream(src, bytes, sink, 4 * cus,
+                                               static_cast<hipStream_t>(stream)),
+                       "pkv_read_stream");
 }
 
 int pkv_validate_metadata(const int32_t* page_table, const int32_t* context_lens,

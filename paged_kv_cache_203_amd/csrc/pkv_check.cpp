@@ -299,7 +299,7 @@ StepWorkspace step_workspace(const pkv_shape& s, int64_t groups, int heads_per_w
   const uint64_t head_groups = uint64_t(s.num_kv_heads / heads_per_wg);
   StepWorkspace w;
   w.count_off = 0;
-  w.out_off = up(uint64_t(kMaxStepBatch) * head_groups * 4);
+  w.out_off = up(uint64_t(kMaxStepBatch) * head_groups * 8);
   w.lse_off = w.out_off + up(pieces * s.num_q_heads * s.head_dim * 4);
   w.bytes = w.lse_off + up(pieces * s.num_q_heads * 4);
   return w;

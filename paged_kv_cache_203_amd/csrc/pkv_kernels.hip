@@ -31,6 +31,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "pkv_arrival.h"
 #include "pkv_device.h"
 #include "pkv_launch.h"
 
@@ -722,6 +723,17 @@ struct StepSplit {
   }
 };
 
+// A piece of `tiles` tiles arrives on its sequence's counter (pkv_arrival.h): the word is first
+// raised to this call's floor, so that a count an earlier call left behind starts again from zero,
+// then the tiles are added.  Returns the tiles this call had counted before.
+__device__ inline int arrive(uint64_t* counter, uint32_t generation, int tiles) {
+  __hip_atomic_fetch_max(counter, arrival_floor(generation), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t old = __hip_atomic_fetch_add(counter, uint64_t(tiles), __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+  return int(arrival_count(old));
+}
+
 // Exclusive prefix sum of the weights 4 * step_tiles(b) + su over the batch into `wpre`
 // (B + 1 entries).  `scan` is NT / 64 ints of scratch (or more).  All threads of the block take
 // part.
@@ -1006,8 +1018,7 @@ __global__ __launch_bounds__(NW * 64) void step_kernel(const StepParams p) {
     if (early_b < 0 || early_tiles == 0) return;
     __syncthreads();   // every wave's partial stores have completed
     if (threadIdx.x == 0)
-      early_ret = __hip_atomic_fetch_add(&p.ws_count[int64_t(early_b) * nhg + hg], early_tiles,
-                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      early_ret = arrive(&p.ws_count[int64_t(early_b) * nhg + hg], p.generation, early_tiles);
     early_tiles = 0;
   };
   while (true) {
@@ -1072,11 +1083,21 @@ __global__ __launch_bounds__(NW * 64) void step_kernel(const StepParams p) {
 
   // Count the split pieces' tiles in (at most two pieces: the range's first and last; the first
   // one was usually counted already, see count_first); the workgroup that brings a sequence's
-  // count to its number of tiles merges all of its pieces.  The partials were written, and are
-  // read, with device-scope accesses, which are coherent across the XCDs (each has its own L2)
-  // without an L2 write-back or invalidate: each thread waits until its stores are complete,
-  // the barrier orders that before the increments, and a merging workgroup issues its loads
-  // only after it has read the final count.
+  // count to its number of tiles merges all of its pieces.
+  // The hand-off between workgroups, which may run on different XCDs (each XCD's L2 is not
+  // coherent with the others), is the agent-scope release / acquire pattern of the AMDGPU memory
+  // model without its cache maintenance, which has nothing to act on here:
+  //  * producer: the partials are agent-scope relaxed atomic stores (global/buffer stores with
+  //    sc1, written through to the device's coherence point); s_waitcnt vmcnt(0) waits until
+  //    every one of this thread's stores is complete; the barrier (a workgroup fence plus
+  //    s_barrier, which the compiler does not move memory operations across) orders all threads'
+  //    completed stores before thread 0's agent-scope counter update (global atomics with sc1);
+  //  * consumer: the merging workgroup reads the final count from its own update's return value,
+  //    passes a barrier, and only then issues its loads of the partials, as agent-scope relaxed
+  //    atomic loads (sc1), which return the value at the coherence point, not an L2 copy.
+  // A release would add buffer_wbl2 (write back L2 lines that plain stores dirtied) and an acquire
+  // buffer_inv (drop L2 lines that plain loads could hit); the partials are never written or read
+  // by plain accesses, so the write-back and the invalidate are not needed.
   if (split_first < 0 && split_last < 0) return;
   wait_vmcnt<0>();
   __syncthreads();
@@ -1087,8 +1108,7 @@ __global__ __launch_bounds__(NW * 64) void step_kernel(const StepParams p) {
     if (sb >= 0) {
       const bool counted = threadIdx.x == 0 && early_b == sb && early_tiles == 0;
       const int old = counted ? early_ret
-                              : __hip_atomic_fetch_add(&p.ws_count[int64_t(sb) * nhg + hg], tiles,
-                                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                              : arrive(&p.ws_count[int64_t(sb) * nhg + hg], p.generation, tiles);
       last = old + tiles == prefix(sb + 1) - prefix(sb);
     }
     merging[threadIdx.x] = last;
@@ -1099,7 +1119,7 @@ __global__ __launch_bounds__(NW * 64) void step_kernel(const StepParams p) {
     if (!merging[i]) continue;
     step_merge<DT, D, NW * 64>(p, sp, sb, hg, HPW * a.group, prefix(sb), prefix(sb + 1), scan);
     if (threadIdx.x == 0)   // ready for the next call
-      __hip_atomic_store(&p.ws_count[int64_t(sb) * nhg + hg], 0, __ATOMIC_RELAXED,
+      __hip_atomic_store(&p.ws_count[int64_t(sb) * nhg + hg], uint64_t(0), __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
   }
 }

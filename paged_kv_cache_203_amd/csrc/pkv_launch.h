@@ -30,9 +30,9 @@ struct DecodeParams {
 
 // Balanced decode step: `a` carries the attention arguments (heads_per_wg set; the partition
 // fields are unused).  Workspace (laid out by step_workspace): per-(sequence, head group)
-// counters of the tiles whose pieces have arrived, ws_count (zero before the first call; every
-// call leaves them at zero), piece partials ws_out [(groups + B) * Hq * D] and ws_lse
-// [(groups + B) * Hq].
+// arrival counters ws_count (generation-tagged words, see pkv_arrival.h; zero before the first
+// call, and every completed call leaves them at zero), piece partials ws_out
+// [(groups + B) * Hq * D] and ws_lse [(groups + B) * Hq].
 struct StepParams {
   DecodeParams a;
   const void* k_new;     // null: no append
@@ -41,7 +41,8 @@ struct StepParams {
   void* v_pool_w;
   float* ws_out;
   float* ws_lse;
-  int32_t* ws_count;
+  uint64_t* ws_count;
+  uint32_t generation;   // this call's generation (pkv_arrival.h), never 0
   void* out;
   float* lse_out;        // may be null
   int32_t groups;        // token-range groups per head group
@@ -146,5 +147,9 @@ hipError_t launch_append(const AppendParams& p, hipStream_t stream);
 hipError_t launch_rope_append(const RopeParams& p, int dtype, int head_dim, hipStream_t stream);
 hipError_t launch_validate(const ValidateParams& p, hipStream_t stream);
 hipError_t launch_copy_pages(const CopyPagesParams& p, hipStream_t stream);
+// Plain read stream of `bytes` (a multiple of 16) from `src` over `workgroups` workgroups; each
+// folds what it read into *sink (XOR).
+hipError_t launch_read_stream(const void* src, uint64_t bytes, uint32_t* sink, int workgroups,
+                              hipStream_t stream);
 
 }  // namespace pkv

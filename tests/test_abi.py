@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 29, names
+    assert len(names) == 30, names
     for n in names:
         assert hasattr(L.lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True, text=True).stdout
@@ -231,3 +231,12 @@ def test_copy_pages_rejections(L):
     assert cp(k=FAKE + 0x100004) == -2
     assert cp(v=FAKE + 0x100000) == -1          # the pools overlap
     assert cp(n=0, pairs=0) == 0                # nothing to copy
+
+
+def test_read_stream_rejections(L):
+    import ctypes
+    sink = ctypes.c_uint32(0)
+    assert L.lib.pkv_read_stream(None, 16, ctypes.addressof(sink), None) == -1
+    assert L.lib.pkv_read_stream(FAKE, 16, None, None) == -1
+    assert L.lib.pkv_read_stream(FAKE + 8, 16, FAKE, None) == -1   # misaligned
+    assert L.lib.pkv_read_stream(FAKE, 24, FAKE, None) == -1       # not whole 16 B

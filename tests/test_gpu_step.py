@@ -203,6 +203,32 @@ def test_step_repeated_calls_bitwise_stable(pkv):
                 assert torch.equal(outs[j].view(torch.int16), first[j].view(torch.int16)), (rep, j)
 
 
+def test_step_discards_counters_left_by_an_earlier_call(pkv):
+    """Arrival counters that an earlier call left part-way (here planted: every counter set to a
+    non-zero count under an older generation) are started afresh by the next call, which must
+    give the same bits as on a clean workspace."""
+    w = W.make_workload(W.config(2).scaled(batch=24, lengths=("uniform", 300, 2500)))
+    d = DeviceWorkload(w)
+    ws = torch.zeros(pkv.decode_step_workspace_bytes(d.q, d.k_pool, d.page_table),
+                     dtype=torch.uint8, device="cuda")
+    clean = pkv.paged_decode_step(d.q, d.k_pool, d.v_pool, d.page_table, d.context_lens, d.scale,
+                                  workspace=ws)
+    for _ in range(3):   # later calls take generations above the one planted below
+        pkv.paged_decode_step(d.q, d.k_pool, d.v_pool, d.page_table, d.context_lens, d.scale,
+                              workspace=ws)
+    torch.cuda.synchronize()
+    nhg = 1   # eight KV heads: one head group
+    words = ws[:w.cfg.batch * nhg * 8].view(torch.int64)
+    words.fill_((1 << 32) | 5)   # generation 1, five tiles already counted
+    out = pkv.paged_decode_step(d.q, d.k_pool, d.v_pool, d.page_table, d.context_lens, d.scale,
+                                workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), clean.view(torch.int16))
+    # the counters the call used (those of split sequences) are left at zero; the rest untouched
+    planted = (1 << 32) | 5
+    assert bool(((words == 0) | (words == planted)).all()) and int((words == 0).sum()) > 0
+
+
 STEP_SHAPES = [  # (Hkv, G, D, PS, dtype, max length): one wave per KV head (Hkv % 8 == 0) or
     # several (Hkv 1, 2, 4), two head groups per range (Hkv 16), every padded group size, both
     # head sizes, fp32 with head_dim 128 (one tile in flight), pages of 16 to 256 tokens.  Waves
