@@ -266,6 +266,20 @@ int pkv_paged_decode_step(const void* q, const void* k_new, const void* v_new, v
                           float scale, void* workspace, size_t workspace_bytes, void* out,
                           float* lse_out, const pkv_shape* shape, void* stream);
 
+/* pkv_paged_decode_step for callers that cannot allocate or hand over a workspace (code being
+ * captured into a graph, tight serving loops, harnesses that forbid allocation): the same kernel,
+ * its workspace taken from a static device array of the library (64 MiB, held on every GPU the
+ * library runs on until the process ends) instead of a caller buffer.  Arguments, results and
+ * bits are those of pkv_paged_decode_step with the same inputs.  The call allocates nothing; on
+ * its first use on a device it looks up the array's device address and clears it with one kernel
+ * on `stream`.  Shapes whose step workspace (pkv_decode_step_workspace_bytes) exceeds 64 MiB are
+ * rejected with PKV_EWORKSPACE.  Every call on one GPU shares that GPU's array: calls that
+ * overlap on one GPU (other streams, other threads) race and must be serialised by the caller. */
+int pkv_paged_decode_step_noalloc(const void* q, const void* k_new, const void* v_new,
+                                  void* k_pool, void* v_pool, const int32_t* page_table,
+                                  const int32_t* context_lens, float scale, void* out,
+                                  float* lse_out, const pkv_shape* shape, void* stream);
+
 /* The decode step with the rotary embedding fused in: as pkv_paged_decode_step with an append,
  * except that the new key is written rotated, and the query rotated, both at position
  * context_lens[b], exactly as pkv_rope_kv_append computes them (same float32 steps, same

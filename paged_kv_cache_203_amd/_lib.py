@@ -54,6 +54,9 @@ _SIGNATURES = {
     "pkv_paged_decode_step": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float,
                                              _vp, ctypes.c_size_t, _vp, _vp,
                                              ctypes.POINTER(PkvShape), _vp]),
+    "pkv_paged_decode_step_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                                     ctypes.c_float, _vp, _vp,
+                                                     ctypes.POINTER(PkvShape), _vp]),
     "pkv_paged_decode_cascade": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _vp, _vp, ctypes.c_float,
                                                 _i32, _vp, _vp, _i32, _vp, _vp,
                                                 ctypes.POINTER(PkvShape), _vp]),
@@ -411,6 +414,33 @@ def paged_decode_step(q, k_pool, v_pool, page_table, context_lens, scale: Option
         None if v_new is None else v_new.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
         page_table.data_ptr(), context_lens.data_ptr(), scale, workspace.data_ptr(),
         workspace.numel(), out.data_ptr(), lse_ptr, ctypes.byref(s), _stream(q.device)))
+    return out
+
+
+def paged_decode_step_noalloc(q, k_pool, v_pool, page_table, context_lens, out, scale=None,
+                              k_new=None, v_new=None, lse_out=None):
+    """paged_decode_step with the library's static device scratch as its workspace (the C call
+    allocates nothing; ``out`` is the caller's).  Same results as paged_decode_step."""
+    torch = _torch()
+    s = _attention_shape(q, k_pool, v_pool, page_table, context_lens)
+    if (k_new is None) != (v_new is None):
+        raise ValueError("k_new and v_new must both be given or both be None")
+    if k_new is not None:
+        for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+            _require(t, n, dtype=q.dtype, ndim=3, device=q.device)
+            if tuple(t.shape) != (s.batch, s.num_kv_heads, s.head_dim):
+                raise ValueError(f"{n} must be [B, Hkv, D]")
+    _require(out, "out", dtype=q.dtype, ndim=3, device=q.device)
+    lse_ptr = None
+    if lse_out is not None:
+        _require(lse_out, "lse_out", dtype=torch.float32, ndim=2, device=q.device)
+        lse_ptr = lse_out.data_ptr()
+    scale = _default_scale(s.head_dim) if scale is None else float(scale)
+    _check(lib.pkv_paged_decode_step_noalloc(
+        q.data_ptr(), None if k_new is None else k_new.data_ptr(),
+        None if v_new is None else v_new.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+        page_table.data_ptr(), context_lens.data_ptr(), scale, out.data_ptr(), lse_ptr,
+        ctypes.byref(s), _stream(q.device)))
     return out
 
 

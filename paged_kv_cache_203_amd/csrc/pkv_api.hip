@@ -5,6 +5,7 @@
 
 #include <atomic>
 #include <cmath>
+#include <mutex>
 #include <string>
 
 #include "../../include/pkv.h"
@@ -336,6 +337,82 @@ int pkv_paged_decode_step(const void* q, const void* k_new, const void* v_new, v
   return decode_step("pkv_paged_decode_step", q, k_new, v_new, k_pool, v_pool, page_table,
                      context_lens, nullptr, nullptr, 0, scale, workspace, workspace_bytes, out,
                      lse_out, shape, stream);
+}
+
+}  // extern "C"
+
+// Scratch of pkv_paged_decode_step_noalloc: the step's workspace (arrival counters, piece partials)
+// in a static device array, for callers that cannot allocate.  Each GPU the library runs on holds
+// its own copy until the process ends.  In host code `scratch` only names the symbol; its device
+// address is looked up once per device (scratch_on_device) and only that address is used.
+constexpr size_t kStepScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) char scratch[kStepScratchBytes];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+
+struct ScratchSlot {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+  bool cleared = false;   // the zeroing launch has been enqueued
+};
+ScratchSlot g_scratch_slots[kMaxScratchDevices];
+std::mutex g_scratch_clear;
+
+// The device address of `scratch` on `dev` (the current device): looked up on first use.
+hipError_t scratch_on_device(int dev, void** ptr) {
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  ScratchSlot& s = g_scratch_slots[dev];
+  std::call_once(s.once, [&] { s.err = hipGetSymbolAddress(&s.ptr, HIP_SYMBOL(scratch)); });
+  *ptr = s.ptr;
+  return s.err;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_paged_decode_step_noalloc(const void* q, const void* k_new, const void* v_new,
+                                  void* k_pool, void* v_pool, const int32_t* page_table,
+                                  const int32_t* context_lens, float scale, void* out,
+                                  float* lse_out, const pkv_shape* shape, void* stream) {
+  const char* name = "pkv_paged_decode_step_noalloc";
+  std::string msg;
+  int rc = pkv::check_shape(shape, msg);
+  if (rc) return set_error(rc, std::string(name) + ": " + msg);
+  if (shape->batch == 0) return PKV_OK;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return set_error(PKV_ELAUNCH, std::string(name) + ": no device");
+  const int64_t groups = step_groups(*shape);
+  const uint64_t need =
+      groups ? pkv::step_workspace(*shape, groups, heads_per_workgroup(shape->num_kv_heads)).bytes : 0;
+  if (need > kStepScratchBytes)
+    return set_error(PKV_EWORKSPACE, std::string(name) + ": this shape needs " + std::to_string(need) +
+                                         " bytes of step workspace, more than the " +
+                                         std::to_string(kStepScratchBytes) +
+                                         "-byte static scratch; use pkv_paged_decode_step with a "
+                                         "workspace of that size");
+  void* ptr = nullptr;
+  const hipError_t e = scratch_on_device(dev, &ptr);
+  if (e != hipSuccess)
+    return set_error(PKV_ELAUNCH, std::string(name) + ": device address of the scratch: " +
+                                      hipGetErrorString(e));
+  {
+    // The arrival counters must start at zero: the scratch is cleared once per device, on the
+    // first call's stream, ahead of that call (later calls leave the counters at zero).
+    std::lock_guard<std::mutex> lock(g_scratch_clear);
+    ScratchSlot& s = g_scratch_slots[dev];
+    if (!s.cleared) {
+      (void)hipGetLastError();
+      const int r = launch_status(pkv::launch_zero(ptr, kStepScratchBytes, static_cast<hipStream_t>(stream)), name);
+      if (r) return r;
+      s.cleared = true;
+    }
+  }
+  return decode_step(name, q, k_new, v_new, k_pool, v_pool, page_table, context_lens, nullptr,
+                     nullptr, 0, scale, ptr, kStepScratchBytes, out, lse_out, shape, stream);
 }
 
 int pkv_paged_decode_step_rope(const void* q, const void* k_new, const void* v_new, void* k_pool,

@@ -1197,6 +1197,13 @@ __global__ __launch_bounds__(256) void copy_pages_kernel(const CopyPagesParams p
   }
 }
 
+// Zero `words` 16-byte words from `dst` (vector stores; used instead of a memset so that the
+// clearing is an ordinary kernel node when a caller captures the stream).
+__global__ __launch_bounds__(256) void zero_kernel(u32x4* dst, uint64_t words) {
+  for (uint64_t i = uint64_t(blockIdx.x) * 256 + threadIdx.x; i < words; i += uint64_t(gridDim.x) * 256)
+    dst[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
 // One workgroup checks every row and writes the status word (no pre-clearing needed).
 __global__ __launch_bounds__(1024) void validate_kernel(const ValidateParams p) {
   __shared__ int status;
@@ -1348,6 +1355,15 @@ hipError_t launch_append(const AppendParams& p, hipStream_t stream) {
 hipError_t launch_copy_pages(const CopyPagesParams& p, hipStream_t stream) {
   if (p.n == 0) return hipSuccess;
   hipLaunchKernelGGL(copy_pages_kernel, dim3(unsigned(p.n)), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero(void* dst, uint64_t bytes, hipStream_t stream) {
+  const uint64_t words = bytes / 16;
+  if (words == 0) return hipSuccess;
+  const uint64_t blocks = (words + 255) / 256;
+  hipLaunchKernelGGL(zero_kernel, dim3(unsigned(blocks < 1024 ? blocks : 1024)), dim3(256), 0,
+                     stream, static_cast<u32x4*>(dst), words);
   return hipGetLastError();
 }
 

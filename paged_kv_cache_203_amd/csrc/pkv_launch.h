@@ -147,6 +147,8 @@ hipError_t launch_append(const AppendParams& p, hipStream_t stream);
 hipError_t launch_rope_append(const RopeParams& p, int dtype, int head_dim, hipStream_t stream);
 hipError_t launch_validate(const ValidateParams& p, hipStream_t stream);
 hipError_t launch_copy_pages(const CopyPagesParams& p, hipStream_t stream);
+// Zero `bytes` (a multiple of 16) of device memory at `dst` (16-byte aligned) with a kernel.
+hipError_t launch_zero(void* dst, uint64_t bytes, hipStream_t stream);
 // Plain read stream of `bytes` (a multiple of 16) from `src` over `workgroups` workgroups; each
 // folds what it read into *sink (XOR).
 hipError_t launch_read_stream(const void* src, uint64_t bytes, uint32_t* sink, int workgroups,
