@@ -1091,7 +1091,8 @@ __global__ __launch_bounds__(NW * 64) void step_kernel(const StepParams p) {
   //    sc1, written through to the device's coherence point); s_waitcnt vmcnt(0) waits until
   //    every one of this thread's stores is complete; the barrier (a workgroup fence plus
   //    s_barrier, which the compiler does not move memory operations across) orders all threads'
-  //    completed stores before thread 0's agent-scope counter update (global atomics with sc1);
+  //    completed stores before thread 0's agent-scope counter update (relaxed agent-scope
+  //    atomicrmw: global_atomic_umax / global_atomic_add, which act at agent scope as emitted);
   //  * consumer: the merging workgroup reads the final count from its own update's return value,
   //    passes a barrier, and only then issues its loads of the partials, as agent-scope relaxed
   //    atomic loads (sc1), which return the value at the coherence point, not an L2 copy.
