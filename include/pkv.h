@@ -377,8 +377,9 @@ const char* pkv_pages_last_error(void);
 size_t pkv_partial_workspace_bytes(const pkv_shape* shape, int32_t max_partitions);
 
 /* Plain read stream, for measurement: every byte of src[0, bytes) is read once with 16-byte
- * loads spread over the whole device, and the words read are folded by XOR into *sink (a device
- * uint32, not cleared here).  Its rate is the read bandwidth this device actually reaches, the
+ * loads spread over the whole device (the direct-to-LDS loads the decode kernels stream K rows
+ * with), and one 32-bit word per workgroup of what was read is folded by XOR into *sink (a device
+ * uint32, not cleared here), so that no read is dead.  Its rate is the read bandwidth this device actually reaches, the
  * ceiling the decode calls' algorithmic bytes per second are reported against beside the
  * published HBM peak (the CacheIR page, "Latest local validation", reports a bandwidth
  * calibration beside its kernel timings).  src and bytes must be multiples of 16

@@ -533,8 +533,8 @@ def copy_pages(k_pool, v_pool, pairs) -> None:
 
 def read_stream(buf, sink) -> None:
     """Read every byte of the contiguous device tensor ``buf`` once (measurement of the device's
-    read bandwidth); the words read are folded by XOR into ``sink`` (a device int32 tensor of one
-    element or more, first element used)."""
+    read bandwidth); one word per workgroup of what was read is folded by XOR into ``sink`` (a
+    device int32 tensor of one element or more, first element used)."""
     torch = _torch()
     _require(buf, "buf")
     _require(sink, "sink", dtype=torch.int32, device=buf.device)

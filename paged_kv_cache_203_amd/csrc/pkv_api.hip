@@ -542,8 +542,8 @@ int pkv_read_stream(const void* src, size_t bytes, uint32_t* sink, void* stream)
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     return set_error(PKV_ELAUNCH, "pkv_read_stream: no device");
   (void)hipGetLastError();
-  // Four 8-wave workgroups per compute unit: every SIMD keeps eight waves of loads in flight.
-  return launch_status(pkv::launch_read_stream(src, bytes, sink, 4 * cus,
+  // One 8-wave workgroup per compute unit, each wave with 16 KB of loads in flight.
+  return launch_status(pkv::launch_read_stream(src, bytes, sink, cus,
                                                static_cast<hipStream_t>(stream)),
                        "pkv_read_stream");
 }

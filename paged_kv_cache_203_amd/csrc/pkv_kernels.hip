@@ -735,10 +735,11 @@ __device__ inline int arrive(uint64_t* counter, uint32_t generation, int tiles) 
 }
 
 // Exclusive prefix sum of the weights 4 * step_tiles(b) + su over the batch into `wpre`
-// (B + 1 entries).  `scan` is NT / 64 ints of scratch (or more).  All threads of the block take
-// part.
+// (B + 1 entries), and the tokens attended in each sequence's last tile (1..16) into `tail`, so
+// that no later step needs the lengths from global memory.  `scan` is NT / 64 ints of scratch
+// (or more).  All threads of the block take part.
 template <int NT>
-__device__ void weight_prefix(const StepParams& p, int su, int* wpre, int* scan) {
+__device__ void weight_prefix(const StepParams& p, int su, int* wpre, uint8_t* tail, int* scan) {
   const int B = p.a.batch;
   const int tid = threadIdx.x;
   const int seg = (B + NT - 1) / NT;
@@ -762,7 +763,9 @@ __device__ void weight_prefix(const StepParams& p, int su, int* wpre, int* scan)
   int run = before + incl - local;
   for (int b = lo; b < hi; ++b) {
     wpre[b] = run;
-    run += 4 * step_tiles(p, b) + su;
+    const int n = step_tiles(p, b);
+    run += 4 * n + su;
+    tail[b] = uint8_t(n > 0 ? p.a.context_lens[b] + p.append - (n - 1) * kTile : 0);
   }
   if (tid == NT - 1) wpre[B] = total;
   __syncthreads();
@@ -862,6 +865,7 @@ __global__ __launch_bounds__(NW * 64) void step_kernel(const StepParams p) {
   static_assert((DEPTH - 1) * Geo::LOADS < 64, "vmcnt range");
   __shared__ Shm sm;
   __shared__ int wpre[kMaxStepBatch + 1];
+  __shared__ uint8_t ltail[kMaxStepBatch];   // tokens attended in each sequence's last tile
   __shared__ int scan[NW * 64];
 
   const DecodeParams& a = p.a;
@@ -890,7 +894,7 @@ __global__ __launch_bounds__(NW * 64) void step_kernel(const StepParams p) {
   int first_tiles = 0, last_tiles = 0;      // ... and the tiles of those pieces
 
   const int su = start_units(WPH);
-  weight_prefix<NW * 64>(p, su, wpre, scan);
+  weight_prefix<NW * 64>(p, su, wpre, ltail, scan);
   const int B = a.batch;
   const StepSplit sp{wpre, B, wpre[B], p.groups, su};
   auto prefix = [&](int x) { return sp.tiles_before(x); };   // tiles of the sequences before x
@@ -928,7 +932,9 @@ __global__ __launch_bounds__(NW * 64) void step_kernel(const StepParams p) {
     src.page_stride = a.page_stride;
     src.head_off = kvh * Geo::RB;
     src.t_begin = tb * kTile;
-    src.t_end = min(a.context_lens[bb] + p.append, te * kTile);
+    // tokens attended: (n - 1) whole tiles plus ltail[bb] (n = the sequence's tiles)
+    const int n_bb = prefix(bb + 1) - prefix(bb);
+    src.t_end = te < n_bb ? te * kTile : (n_bb - 1) * kTile + ltail[bb];
     src.sub = qsplit ? 0 : wave / HPW;
     src.stride = qsplit ? 1 : WPH;
     src.keep = qsplit && !part ? 1 : 0;
@@ -938,7 +944,7 @@ __global__ __launch_bounds__(NW * 64) void step_kernel(const StepParams p) {
     src.rope_sin = p.rope_sin;
     src.rope_pos = -1;
     if constexpr (ROPE) {
-      const int L = a.context_lens[bb];   // the new token's position
+      const int L = (n_bb - 1) * kTile + ltail[bb] - 1;   // the new token's position
       src.rope_pos = L >= 0 && L < p.rope_rows ? L : -1;
     }
     return src;
@@ -962,7 +968,7 @@ __global__ __launch_bounds__(NW * 64) void step_kernel(const StepParams p) {
     const int row_bytes = a.hkv * Geo::RB;
     for (int bb = b; bb < B && prefix(bb) < hi; ++bb) {
       if (prefix(bb + 1) == prefix(bb) || prefix(bb + 1) > hi) continue;
-      const int L = a.context_lens[bb];
+      const int L = (prefix(bb + 1) - prefix(bb) - 1) * kTile + ltail[bb] - 1;   // the new row's slot
       const int page = a.page_table[int64_t(bb) * a.max_pages + (L >> a.page_shift)];
       if (page < 0 || page >= a.num_pages) continue;
       const int64_t dst = int64_t(page) * a.page_stride +
