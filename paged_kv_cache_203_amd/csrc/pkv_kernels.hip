@@ -1131,13 +1131,21 @@ __global__ __launch_bounds__(NW * 64) void step_kernel(const StepParams p) {
   }
 }
 
-// One wavefront per (sequence, query head): out = sum_p w_p o_p / sum_p w_p, w_p = e^(lse_p - M).
+// One wavefront per (sequence, query head): out = sum_p w_p o_p / sum_p w_p, w_p = e^(lse_p - M),
+// partitions in order.  The loads are batched so that the chain of dependent round trips is
+// short: the first 64 log-sum-exps load together with the length (lane i takes partition i), the
+// maximum is a wave reduction, and then the partial rows of up to kBatch partitions load at once;
+// the weights and the sums are the same sequential ones partition after partition.
 template <int DT, int D>
 __global__ __launch_bounds__(64) void merge_kernel(const MergeParams p) {
   constexpr int DPL = D / 64;   // dims per lane
+  constexpr int kBatch = 16;    // partial rows in flight per lane
   const int lane = threadIdx.x;
   const int b = blockIdx.x / p.hq;   // row (sequence, or sequence x query token)
   const int h = blockIdx.x % p.hq;
+  const int64_t prow = (int64_t(b) * p.hq + h) * p.max_partitions;
+  const float* lse = p.partial_lse + prow;
+  const float lse0 = lane < p.max_partitions ? lse[lane] : neg_inf();   // used below n only
   int L = p.context_lens[p.q_tokens > 1 ? b / p.q_tokens : b];
   if (p.q_tokens > 1 && L > 0 && L <= p.capacity) L = max(L - p.q_tokens + 1 + b % p.q_tokens, 0);
   const int64_t orow = (int64_t(b) * p.hq + h) * D;
@@ -1149,20 +1157,35 @@ __global__ __launch_bounds__(64) void merge_kernel(const MergeParams p) {
     return;
   }
   const int n = (L + p.partition_tokens - 1) / p.partition_tokens;
-  const int64_t prow = (int64_t(b) * p.hq + h) * p.max_partitions;
-  const float* lse = p.partial_lse + prow;
-  float M = neg_inf();
-  for (int i = 0; i < n; ++i) M = fmaxf(M, lse[i]);
+  float M = lane < n ? lse0 : neg_inf();
+  for (int i0 = 64; i0 < n; i0 += 64) M = fmaxf(M, i0 + lane < n ? lse[i0 + lane] : neg_inf());
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
   float wsum = 0.f;
   float acc[DPL];
 #pragma unroll
   for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
-  for (int i = 0; i < n; ++i) {
-    const float w = fast_exp2((lse[i] - M) * kLog2e);
-    wsum += w;
-    const float* po = p.partial_out + (prow + i) * D + lane * DPL;
+  for (int i0 = 0; i0 < n; i0 += 64) {
+    const int cnt = min(64, n - i0);
+    const float lv = i0 == 0 ? lse0 : (lane < cnt ? lse[i0 + lane] : neg_inf());
+    const float wl = lane < cnt ? fast_exp2((lv - M) * kLog2e) : 0.f;   // partition i0 + lane
+    for (int j0 = 0; j0 < cnt; j0 += kBatch) {
+      float v[kBatch][DPL];
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) acc[e] = fmaf(w, po[e], acc[e]);
+      for (int u = 0; u < kBatch; ++u) {   // rows past the partitions repeat the last one
+        const float* po = p.partial_out + (prow + i0 + min(j0 + u, cnt - 1)) * D + lane * DPL;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) v[u][e] = po[e];
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        if (j0 + u >= cnt) break;
+        const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), j0 + u));
+        wsum += w;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) acc[e] = fmaf(w, v[u][e], acc[e]);
+      }
+    }
   }
 #pragma unroll
   for (int e = 0; e < DPL; ++e) store_elem<DT>(p.out, orow + lane * DPL + e, acc[e] / wsum);
