@@ -51,13 +51,33 @@ int heads_per_workgroup(int hkv) {
   return best;
 }
 
+// KV heads per workgroup of the balanced decode step: as many as divide both hkv and the wave
+// count, then halved while some wave would hold more than four query heads (larger groups need
+// the 8- and 16-column score tiles, whose accumulators do not fit the register budget without
+// spills); with fewer heads per workgroup, the waves that share a KV head split its query heads.
+int step_heads_per_workgroup(int hkv, int group) {
+  const int waves = pkv::decode_waves();
+  int h = heads_per_workgroup(hkv);
+  while (h > 1) {
+    const int wph = waves / h;
+    const int gw = (group + wph - 1) / wph;
+    const bool split = wph > 1 && (wph - 1) * gw < group;
+    if ((split ? gw : group) <= 4) break;
+    h /= 2;
+  }
+  return h;
+}
+int step_heads_per_workgroup(const pkv_shape& s) {
+  return step_heads_per_workgroup(s.num_kv_heads, s.num_q_heads / s.num_kv_heads);
+}
+
 // Workgroup ranges of the balanced decode step on the current device: one 8-wave workgroup per
 // compute unit, shared among the KV-head groups.  0 when no device is available.
 int64_t step_groups(const pkv_shape& s) {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  const int nhg = s.num_kv_heads / heads_per_workgroup(s.num_kv_heads);
+  const int nhg = s.num_kv_heads / step_heads_per_workgroup(s);
   return cus / nhg > 0 ? cus / nhg : 1;
 }
 
@@ -277,7 +297,7 @@ size_t pkv_decode_step_workspace_bytes(const pkv_shape* shape) {
   if (pkv::check_shape(shape, msg) != PKV_OK) return 0;
   const int64_t groups = step_groups(*shape);
   if (groups == 0) return 0;
-  return size_t(pkv::step_workspace(*shape, groups, heads_per_workgroup(shape->num_kv_heads)).bytes);
+  return size_t(pkv::step_workspace(*shape, groups, step_heads_per_workgroup(*shape)).bytes);
 }
 
 namespace {
@@ -291,7 +311,7 @@ int decode_step(const char* name, const void* q, const void* k_new, const void* 
   if (rc) return set_error(rc, std::string(name) + ": " + msg);
   const int64_t groups = shape->batch ? step_groups(*shape) : 1;
   const pkv::StepWorkspace ws =
-      pkv::step_workspace(*shape, groups ? groups : 1, heads_per_workgroup(shape->num_kv_heads));
+      pkv::step_workspace(*shape, groups ? groups : 1, step_heads_per_workgroup(*shape));
   rc = pkv::check_step(q, k_new, v_new, k_pool, v_pool, page_table, context_lens, scale, workspace,
                        workspace_bytes, groups ? ws.bytes : 0, out, lse_out, shape, msg);
   if (!rc && rope_cos)
@@ -301,7 +321,7 @@ int decode_step(const char* name, const void* q, const void* k_new, const void* 
   if (shape->batch == 0) return PKV_OK;
   pkv::StepParams p{};
   p.a = decode_params(q, k_pool, v_pool, page_table, context_lens, scale, *shape);
-  p.a.heads_per_wg = heads_per_workgroup(p.a.hkv);
+  p.a.heads_per_wg = step_heads_per_workgroup(*shape);
   p.k_new = k_new;
   p.v_new = v_new;
   p.k_pool_w = k_pool;
@@ -387,7 +407,7 @@ int pkv_paged_decode_step_noalloc(const void* q, const void* k_new, const void* 
   if (hipGetDevice(&dev) != hipSuccess) return set_error(PKV_ELAUNCH, std::string(name) + ": no device");
   const int64_t groups = step_groups(*shape);
   const uint64_t need =
-      groups ? pkv::step_workspace(*shape, groups, heads_per_workgroup(shape->num_kv_heads)).bytes : 0;
+      groups ? pkv::step_workspace(*shape, groups, step_heads_per_workgroup(*shape)).bytes : 0;
   if (need > kStepScratchBytes)
     return set_error(PKV_EWORKSPACE, std::string(name) + ": this shape needs " + std::to_string(need) +
                                          " bytes of step workspace, more than the " +
