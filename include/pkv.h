@@ -140,13 +140,15 @@ int pkv_lse_merge(const float* partial_out, const float* partial_lse,
  * (prefix_pages holds prefix_tokens / PS page ids; the page tables' first prefix_tokens / PS
  * entries are not read); tokens t >= prefix_tokens are found through page_table as usual.  The
  * result is that of pkv_paged_decode_attention over L_b = context_lens[b] tokens (rows with
- * L_b < prefix_tokens attend to their first L_b prefix tokens only), computed as three launches
+ * L_b < prefix_tokens attend to their first L_b prefix tokens only), computed as two launches
  * on `stream`:
- *   1. the prefix partitions p < prefix_tokens / P (P = partition_tokens): for each KV head, the
- *      query rows of all sequences (B x G rows) attend to the prefix as one dense product on the
- *      matrix cores, so each prefix page is read once per 128 query rows, not once per sequence;
- *   2. the remaining partitions, as pkv_paged_decode_attention_partial computes them;
- *   3. the merge of all ceil(L_b / P) partitions, as pkv_lse_merge.
+ *   1. one grid holding both kinds of partition, which share no data and run side by side:
+ *      - the prefix partitions p < prefix_tokens / P (P = partition_tokens): for each KV head,
+ *        the query rows of all sequences (B x G rows) attend to the prefix as one dense product
+ *        on the matrix cores, so each prefix page is read once per 128 query rows, not once per
+ *        sequence;
+ *      - the remaining partitions, as pkv_paged_decode_attention_partial computes them;
+ *   2. the merge of all ceil(L_b / P) partitions, as pkv_lse_merge.
  * partial_out / partial_lse are the caller's workspace in the split layout (their contents after
  * the call are the partitions' partials); out and lse_out (may be NULL) are as for
  * pkv_lse_merge.  This follows the shared prefix-page reuse of the TorchInferno page ("Design

@@ -204,18 +204,17 @@ int pkv_paged_decode_cascade(const void* q, const void* k_pool, const void* v_po
   pp.max_partitions = max_partitions;
   pp.tok_stride = d.tok_stride;
   pp.page_stride = d.page_stride;
-  int r = launch_status(pkv::launch_prefix(pp, shape->dtype, shape->head_dim, st),
-                        "pkv_paged_decode_cascade (prefix)");
-  if (r) return r;
-
+  // The suffix partitions (from partition prefix_tokens / P on) and the prefix partitions in one
+  // grid, then the merge.
   d.partial_out = partial_out;
   d.partial_lse = partial_lse;
   d.partition_tokens = partition_tokens;
   d.max_partitions = max_partitions;
   d.part_begin = prefix_tokens / partition_tokens;
   d.heads_per_wg = heads_per_workgroup(d.hkv);
-  r = launch_status(pkv::launch_decode(d, shape->dtype, shape->head_dim, group_pad(d.group), true, st),
-                    "pkv_paged_decode_cascade (suffix)");
+  const int r = launch_status(pkv::launch_cascade(d, pp, shape->dtype, shape->head_dim,
+                                                  group_pad(d.group), st),
+                              "pkv_paged_decode_cascade (partitions)");
   if (r) return r;
 
   pkv::MergeParams m{};

@@ -34,6 +34,7 @@
 #include "pkv_arrival.h"
 #include "pkv_device.h"
 #include "pkv_launch.h"
+#include "pkv_prefix_body.h"
 
 namespace pkv {
 namespace {
@@ -564,20 +565,20 @@ __device__ void combine_waves(const char* w_lds, int hpw, int wph, int G, int nt
 // One workgroup per (sequence, partition, group of KV heads).  Wave w serves KV head
 // hg * HPW + w % HPW and takes that head's tiles w / HPW, + WPH, ... (HPW heads per workgroup,
 // WPH = NW / HPW waves per head).
+// Workgroup `id` of the grid with its LDS `sm` (a kernel of its own, or part of a fused grid).
 template <int DT, int D, int GP, int NW, int DEPTH, bool PARTIAL>
-__global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams p) {
+__device__ inline void decode_body(const DecodeParams& p, int id,
+                                   DecodeShared<DT, D, GP, NW, DEPTH>& sm) {
   using Geo = TileGeo<DT, D>;
   using Shm = DecodeShared<DT, D, GP, NW, DEPTH>;
   static_assert(GP == 4 || GP == 8 || GP == 16, "padded group");
   static_assert((DEPTH - 1) * Geo::LOADS < 64, "vmcnt range");
-  __shared__ Shm sm;
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = p.group;
   const int HPW = p.heads_per_wg;
   const int WPH = NW / HPW;
 
-  int id = blockIdx.x;
   const int nhg = p.hkv / HPW;
   const int hg = id % nhg;
   id /= nhg;
@@ -635,6 +636,35 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams p) {
           store_elem<DT>(p.out, (int64_t(b) * p.hq + h) * D + d, val);
         }
       });
+}
+
+template <int DT, int D, int GP, int NW, int DEPTH, bool PARTIAL>
+__global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams p) {
+  __shared__ DecodeShared<DT, D, GP, NW, DEPTH> sm;
+  decode_body<DT, D, GP, NW, DEPTH, PARTIAL>(p, blockIdx.x, sm);
+}
+
+// Shared-prefix decode, both kinds of partition in one grid: workgroups [0, n_dec) take the
+// suffix partitions (as decode_kernel's partial mode), [n_pre0, n_pre0 + prefix units) the prefix
+// partitions on the matrix cores (as prefix_kernel); n_pre0 is n_dec rounded up to a multiple of
+// 8, so that a prefix workgroup keeps the XCD (block index mod 8) it has in a grid of its own,
+// and the workgroups in between do nothing.  The two kinds share no data, so they run side by
+// side: blocks are dispatched in index order, and the prefix workgroups take the compute units
+// that the short suffix partitions leave early.  One LDS allocation serves either kind.
+template <int DT, int D, int GP, int NW, int DEPTH>
+__global__ __launch_bounds__(NW * 64) void cascade_kernel(const DecodeParams d, const PrefixParams pp,
+                                                          int n_dec, int n_pre0) {
+  static_assert(NW == kPrefixWaves, "one block size for both kinds of workgroup");
+  union Shared {
+    DecodeShared<DT, D, GP, NW, DEPTH> dec;
+    PrefixShared<D> pre;
+  };
+  __shared__ Shared sm;
+  const int id = blockIdx.x;
+  if (id < n_dec)
+    decode_body<DT, D, GP, NW, DEPTH, true>(d, id, sm.dec);
+  else if (id >= n_pre0)
+    prefix_body<DT, D, NW, kPrefixRowBlocks, false>(pp, id - n_pre0, sm.pre);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -1334,6 +1364,40 @@ struct DecodeLaunch {
   }
 };
 
+// The shared-prefix grid of cascade_kernel: the suffix partitions (decode_kernel's partial mode
+// from d.part_begin), then the prefix partitions (prefix_kernel's grid), from a multiple of 8.
+template <int DT, int D, int GP>
+hipError_t launch_cascade_t(const DecodeParams& d, const PrefixParams& pp, hipStream_t stream) {
+  constexpr int ROWS = PrefixGeo<D, kPrefixWaves, kPrefixRowBlocks>::ROWS;
+  const int64_t n_dec = int64_t(d.batch) * (d.hkv / d.heads_per_wg) *
+                        (d.max_partitions > d.part_begin ? d.max_partitions - d.part_begin : 0);
+  const int64_t tiles = (int64_t(pp.batch) * pp.group + ROWS - 1) / ROWS;
+  const int64_t n_pre = pp.prefix_tokens > 0 ? tiles * pp.hkv * (pp.prefix_tokens / pp.partition_tokens) : 0;
+  const int64_t n_pre0 = n_pre > 0 ? (n_dec + 7) / 8 * 8 : n_dec;
+  const int64_t total = n_pre0 + n_pre;
+  if (total == 0) return hipSuccess;
+  if (total > int64_t(INT32_MAX)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((cascade_kernel<DT, D, GP, kWaves, pipe_depth<DT, D>()>), dim3(unsigned(total)),
+                     dim3(kWaves * 64), 0, stream, d, pp, int(n_dec), int(n_pre0));
+  return hipGetLastError();
+}
+
+struct CascadeArgs {
+  const DecodeParams* d;
+  const PrefixParams* pp;
+};
+
+template <int DT, int D, int GP>
+struct CascadeLaunch {
+  static hipError_t run(const CascadeArgs& a, hipStream_t s, bool) {
+    if constexpr (DT == DT_F32) {
+      return hipErrorInvalidValue;   // no prefix kernel for fp32
+    } else {
+      return launch_cascade_t<DT, D, GP>(*a.d, *a.pp, s);
+    }
+  }
+};
+
 template <int DT, int D, int GP>
 struct StepLaunch {
   static hipError_t run(const StepParams& p, hipStream_t s, bool) { return launch_step_t<DT, D, GP>(p, s); }
@@ -1359,6 +1423,12 @@ int decode_waves() { return kWaves; }
 hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim, int group_pad,
                          bool partial, hipStream_t stream) {
   return dispatch_shape<DecodeLaunch>(p, dtype, head_dim, group_pad, stream, partial);
+}
+
+hipError_t launch_cascade(const DecodeParams& d, const PrefixParams& pp, int dtype, int head_dim,
+                          int group_pad, hipStream_t stream) {
+  if (d.batch == 0) return hipSuccess;
+  return dispatch_shape<CascadeLaunch>(CascadeArgs{&d, &pp}, dtype, head_dim, group_pad, stream, false);
 }
 
 hipError_t launch_step(const StepParams& p, int dtype, int head_dim, int group_pad,

@@ -143,6 +143,11 @@ hipError_t launch_step(const StepParams& p, int dtype, int head_dim, int group_p
                        hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, int dtype, int head_dim, hipStream_t stream);
 hipError_t launch_prefix(const PrefixParams& p, int dtype, int head_dim, hipStream_t stream);
+// Shared-prefix decode, both kinds of partition in one launch: `d` as for launch_decode's
+// partial mode (suffix partitions from d.part_begin), `pp` as for launch_prefix (q_tokens = 0).
+// bf16 and fp16 only.
+hipError_t launch_cascade(const DecodeParams& d, const PrefixParams& pp, int dtype, int head_dim,
+                          int group_pad, hipStream_t stream);
 hipError_t launch_append(const AppendParams& p, hipStream_t stream);
 hipError_t launch_rope_append(const RopeParams& p, int dtype, int head_dim, hipStream_t stream);
 hipError_t launch_validate(const ValidateParams& p, hipStream_t stream);
