@@ -133,6 +133,19 @@ def test_cascade_all_rows_inside_prefix_ignore_unused_prefix_slots(pkv):
     check(pkv, w2, 128, "all rows inside prefix", lens=lens)
 
 
+def test_cascade_prefix_spans_the_whole_table(pkv):
+    """The prefix covers every column of the page table, so no suffix partition exists and the
+    launch holds prefix workgroups only; rows of every length up to the whole prefix."""
+    cfg = W.config(3).scaled(batch=7, lengths=("prefix", 512, 1, 30))
+    w = W.make_workload(cfg)
+    table = np.ascontiguousarray(w.page_table[:, :w.shared_pages])
+    lens = np.random.default_rng(11).integers(1, 513, size=7).astype(np.int32)
+    lens[0] = 512
+    lens[1] = 1
+    w2 = dataclasses.replace(w, page_table=table, context_lens=lens)
+    check(pkv, w2, 128, "prefix spans the table")
+
+
 def test_cascade_without_prefix_is_the_split_path(pkv):
     cfg = W.config(3).scaled(batch=12, lengths=("prefix", 256, 1, 300))
     w = W.make_workload(cfg)
