@@ -142,6 +142,7 @@ int decode_waves();
 hipError_t launch_step(const StepParams& p, int dtype, int head_dim, int group_pad,
                        hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, int dtype, int head_dim, hipStream_t stream);
+// Multi-query decode (p.q_tokens > 0) on the matrix cores; bf16 and fp16 only.
 hipError_t launch_prefix(const PrefixParams& p, int dtype, int head_dim, hipStream_t stream);
 // Shared-prefix decode, both kinds of partition in one launch: `d` as for launch_decode's
 // partial mode (suffix partitions from d.part_begin), `pp` as for launch_prefix (q_tokens = 0).

@@ -1,5 +1,6 @@
-// Launches of the shared-prefix partitions and of multi-query decode on the matrix cores; the
-// kernel body and its design are in pkv_prefix_body.h.
+// Launch of multi-query decode on the matrix cores (the prefix kernel body in its per-sequence
+// mode; the body and its design are in pkv_prefix_body.h, and the shared-prefix partitions run it
+// inside cascade_kernel).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -29,26 +30,18 @@ hipError_t launch_multi_query_t(const PrefixParams& p, hipStream_t stream) {
 
 template <int DT, int D>
 hipError_t launch_prefix_t(const PrefixParams& p, hipStream_t stream) {
-  constexpr int NW = kPrefixWaves, RBW = kPrefixRowBlocks;
-  constexpr int ROWS = PrefixGeo<D, NW, RBW>::ROWS;
-  if (p.q_tokens > 0) {   // multi-query: (row tile, partition, sequence, KV head)
-    // Up to 64 rows (G x T): 4-wave workgroups, two per compute unit, so that two blocks of
-    // K/V are in flight per unit; more rows: 8-wave workgroups of 128 rows.
-    if (int64_t(p.q_tokens) * p.group <= 64) return launch_multi_query_t<DT, D, 4>(p, stream);
-    return launch_multi_query_t<DT, D, 8>(p, stream);
-  }
-  const int64_t tiles = (int64_t(p.batch) * p.group + ROWS - 1) / ROWS;
-  const int64_t units = tiles * p.hkv * (p.prefix_tokens / p.partition_tokens);
-  if (units == 0) return hipSuccess;
-  hipLaunchKernelGGL((prefix_kernel<DT, D, NW, RBW, false>), dim3(unsigned(units)), dim3(NW * 64),
-                     0, stream, p);
-  return hipGetLastError();
+  // (row tile, partition, sequence, KV head).  Up to 64 rows (G x T): 4-wave workgroups, two per
+  // compute unit, so that two blocks of K/V are in flight per unit; more rows: 8-wave workgroups
+  // of 128 rows.
+  if (int64_t(p.q_tokens) * p.group <= 64) return launch_multi_query_t<DT, D, 4>(p, stream);
+  return launch_multi_query_t<DT, D, 8>(p, stream);
 }
 
 }  // namespace
 
 hipError_t launch_prefix(const PrefixParams& p, int dtype, int head_dim, hipStream_t stream) {
-  if (p.batch == 0 || (p.q_tokens == 0 && p.prefix_tokens == 0)) return hipSuccess;
+  if (p.q_tokens <= 0) return hipErrorInvalidValue;   // the shared prefix runs in cascade_kernel
+  if (p.batch == 0) return hipSuccess;
   switch (dtype) {
     case DT_BF16:
       return head_dim == 64 ? launch_prefix_t<DT_BF16, 64>(p, stream)
