@@ -7,14 +7,15 @@
 //  * K rows are copied global -> LDS with 16-byte direct-to-LDS loads, 16 lanes per row, so every
 //    load instruction reads whole rows.  In LDS, slice j of token t sits at j ^ (t & SWZ), which
 //    keeps the MFMA-layout reads below free of bank conflicts.
-//  * V rows are loaded into registers the same way (16 lanes per row), in the layout PV uses.
+//  * V rows are copied to LDS the same way (row-major, not swizzled); for PV each lane reads the
+//    dims it accumulates of one token row at a time.
 //  * S^T (16 tokens x 16 head slots) = K_tile . Q^T on MFMA: the G query heads of the GQA group
 //    (zero-padded to 16 columns) share every K row read.
 //  * Online softmax in the MFMA output layout (lane l: tokens 4(l/16)..+3 of head l % 16), base 2.
 //  * p goes through a per-wave LDS slot to the PV layout; PV accumulates in float32 on VALU, so
 //    probabilities are never rounded to 16 bits.
-//  * DEPTH tiles are in flight per wave (K stages in LDS, V in registers), waited for with
-//    explicit vmcnt counts.
+//  * DEPTH tiles are in flight per wave (K and V stages in LDS), waited for with explicit vmcnt
+//    counts; no tile byte passes through registers on its way in.
 // The order in which a token is reduced depends only on its logical position and on the token
 // range a wave is given, never on physical page ids, so results are bitwise invariant under
 // page relabelling and prefix sharing.
@@ -27,6 +28,8 @@
 //    pieces of several sequences.  The workgroup that holds a sequence's last tile first writes
 //    the appended token's K/V rows into the pool, then reads them back with that tile.  The
 //    last workgroup to finish a piece of a sequence merges the sequence's pieces.
+//  * cascade_kernel: shared-prefix decode in one grid, the suffix partitions (decode_kernel's
+//    partial mode) and then the prefix partitions on the matrix cores (pkv_prefix_body.h).
 //  * merge kernels: log-sum-exp combination of partial results.
 #include <hip/hip_runtime.h>
 #include <stdint.h>

@@ -23,8 +23,10 @@
 // Loads of block n + 1 are in flight while block n is computed (two LDS buffers); the rows'
 // lengths, the partition's page ids and the q operands load together at the start.  Each (row,
 // partition) writes its normalised partial output and log-sum-exp in the split-KV layout; the
-// suffix partitions and the merge are the split path's kernels.  Each output element is its own
-// MFMA dot product and the softmax is per row, so a row's bits do not depend on the other rows.
+// suffix partitions are the split path's partition body, run in the same grid (cascade_kernel),
+// and the merge is the split path's kernel.  The same body in its per-sequence mode is multi-query
+// decode (prefix_kernel).  Each output element is its own MFMA dot product and the softmax is per
+// row, so a row's bits do not depend on the other rows.
 #pragma once
 
 #include <hip/hip_runtime.h>
