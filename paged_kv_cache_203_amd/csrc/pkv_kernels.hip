@@ -689,10 +689,10 @@ __device__ inline int step_tiles(const StepParams& p, int b) {
 // (B + 1 entries, in LDS); the `groups` ranges cut the weighted line [0, WT) evenly, and a range
 // owns the tiles whose weighted start falls in it.  Everything depends on the lengths only.
 // The start weight was measured: three tiles with one wave per KV head (12 units: 113.5 us for
-// the Llama-3-8B-shaped step, against 115.5 us at 8 and 118 us at 4), six when several waves
-// share a head (24 units: 57.8 us for the Qwen2-7B-shaped step with alternating tiles, against
-// 65.5 us at 8; with the query split, 12 and 24 measure the same).
-__device__ inline int start_units(int waves_per_head) { return waves_per_head == 1 ? 12 : 24; }
+// the Llama-3-8B-shaped step, against 115.5 us at 8 and 118 us at 4), four when several waves
+// share a head (16 units: 45.2 us for the Qwen2-7B-shaped step with its pairs of waves sharing
+// stages, against 47.3 at 8, 46.3 at 12, 45.6 at 24 and 45.9 at 32).
+__device__ inline int start_units(int waves_per_head) { return waves_per_head == 1 ? 12 : 16; }
 
 struct StepSplit {
   const int* wpre;
