@@ -215,7 +215,7 @@ def cpu_info():
 
 
 def cpu_threads():
-    """Host threads for the oracle: the affinity cores, capped at 16 (the GPU machine's CPU share)."""
+    """Host threads for the oracle: the affinity cores, capped at 16."""
     return max(1, min(16, cpu_info()["affinity_cores"]))
 
 
