@@ -268,6 +268,15 @@ __device__ inline u32x2 lds_read8(uint32_t lds_addr) {
   return r;
 }
 
+// lds_read8 of lds_addr + OFF, the constant in the instruction's offset field.
+template <int OFF>
+__device__ inline u32x2 lds_read8_at(uint32_t lds_addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+  u32x2 r;
+  asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(r) : "v"(lds_addr), "i"(OFF));
+  return r;
+}
+
 // s_waitcnt lgkmcnt(0) for reads issued with lds_read8/16; each value read is then passed
 // through lds_pin(), which the compiler cannot move above the wait (both are volatile asm), so
 // no use of the value can be scheduled before the data has landed.

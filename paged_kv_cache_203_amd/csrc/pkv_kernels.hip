@@ -7,13 +7,16 @@
 //  * K rows are copied global -> LDS with 16-byte direct-to-LDS loads, 16 lanes per row, so every
 //    load instruction reads whole rows.  In LDS, slice j of token t sits at j ^ (t & SWZ), which
 //    keeps the MFMA-layout reads below free of bank conflicts.
-//  * V rows are copied to LDS the same way (row-major, not swizzled); for PV each lane reads the
-//    dims it accumulates of one token row at a time.
+//  * V rows are copied to LDS the same way (row-major; for 16-bit head_dim 128 the 16-byte chunks
+//    of rows 8..15 of a tile swap halves, which spreads the PV operand reads over all banks).
 //  * S^T (16 tokens x 16 head slots) = K_tile . Q^T on MFMA: the G query heads of the GQA group
 //    (zero-padded to 16 columns) share every K row read.
 //  * Online softmax in the MFMA output layout (lane l: tokens 4(l/16)..+3 of head l % 16), base 2.
-//  * p goes through a per-wave LDS slot to the PV layout; PV accumulates in float32 on VALU, so
-//    probabilities are never rounded to 16 bits.
+//  * PV, for 16-bit K/V and head_dim 128, on MFMA as well: O^T (dims x head slots) += V^T . P,
+//    with P straight from the score registers, each probability as a high and a low 16-bit part
+//    (about 16 significant bits), and V^T cut out of 8-byte LDS reads of four token rows.  For
+//    fp32 and head_dim 64, p goes through a per-wave LDS slot to the PV layout and PV
+//    accumulates in float32 on VALU.  Either way the accumulation is float32.
 //  * DEPTH tiles are in flight per wave (K and V stages in LDS), waited for with explicit vmcnt
 //    counts; no tile byte passes through registers on its way in.
 // The order in which a token is reduced depends only on its logical position and on the token
@@ -115,6 +118,13 @@ struct HeadPipe {
   // 4(c + NKL/2) + kq, half a head further on, in the same lane.
   static constexpr int RW4 = Vec16<DT>::N / 4;   // float4s of cos (or sin) per slice
   static constexpr uint32_t VSTAGE0 = DEPTH * Geo::KTILE;   // LDS offset of V stage 0
+  // PV on the matrix cores (16-bit K/V, head_dim 128): O^T (dims x heads) += V^T . P with
+  // mfma_f32_16x16x32, one 16-dim tile per instruction.  The MFMA's k index 8 kq + u stands for
+  // token 4 kq + u % 4 of the tile, taken once with the high and once with the low 16-bit part of
+  // its probability (u < 4: hi, u >= 4: lo), so P keeps about 16 significant bits and every
+  // probability a lane needs is its own score register.  Otherwise PV is fp32 FMA on the VALU.
+  static constexpr bool MPV = DT != DT_F32 && D == 128;
+  static constexpr int NDT = D / 16;       // 16-dim output tiles (MPV)
 
   // per-lane constants
   int lane, m16, kq;
@@ -122,6 +132,7 @@ struct HeadPipe {
   uint32_t vdma_off[NKL];  // ... and of its V slice (V stages are not swizzled)
   uint32_t rd_off[NKL];    // LDS offset of this lane's MFMA operand slice
   uint32_t v_rd;           // LDS offset (within a V stage) of this lane's dims of row kq
+  uint32_t v_rd2;          // MPV: ... of its second group of dims (see init)
   uint32_t lds_base;       // this wave's K stages, then its V stages
   uint32_t p_lds;          // LDS address of this wave's p[16][GP]: a tile's probabilities
   uint32_t a_lds;          // LDS address of this wave's a[GP]: the tile's rescale factors
@@ -132,7 +143,10 @@ struct HeadPipe {
   int pv_pref;
   bool pref_ready = false;
   f32x4 rope_cs[ROPE ? NKL / 2 : 1][2][RW4];   // prefetched cos, sin of this lane's pairs
-  float m_run, l_run, o[GP][VPL];
+  float m_run, l_run;
+  float o[MPV ? 1 : GP][MPV ? 1 : VPL];
+  // MPV: tile j of O^T; lane (m16, kq) holds head m16, dims 64 (j / 4) + 16 kq + 4 i + j % 4.
+  f32x4 o4[MPV ? NDT : 1];
   bool bad;
 
   __device__ void init(int tok_stride, uint32_t lds, float* p, float* a) {
@@ -144,12 +158,23 @@ struct HeadPipe {
     for (int i = 0; i < NKL; ++i) {
       const int t_in = Geo::TPI * i + d_row;
       dma_off[i] = uint32_t(t_in) * tok_stride + uint32_t(d_pos ^ (t_in & Geo::SWZ)) * 16u;
-      vdma_off[i] = uint32_t(t_in) * tok_stride + uint32_t(d_pos) * 16u;
+      // MPV: slot s of V row t holds 16-byte chunk s ^ 8 ((t >> 3) & 1), so that the PV operand
+      // reads of rows 4 kq + i take the two halves of the banks for kq < 2 and kq >= 2.
+      const int vsw = MPV ? 8 * ((t_in >> 3) & 1) : 0;
+      vdma_off[i] = uint32_t(t_in) * tok_stride + uint32_t(d_pos ^ vsw) * 16u;
     }
 #pragma unroll
     for (int c = 0; c < NKL; ++c)
       rd_off[c] = uint32_t(m16) * Geo::RB + uint32_t((4 * c + kq) ^ (m16 & Geo::SWZ)) * 16u;
-    v_rd = uint32_t(kq) * Geo::RB + uint32_t(m16) * Geo::VB;
+    if constexpr (MPV) {
+      // Dims 64 h + 4 m16 .. + 3 of row 4 kq: chunk 8 h + m16 / 2 at slot 8 (h ^ (kq >> 1)) + m16 / 2.
+      const uint32_t row = uint32_t(4 * kq) * Geo::RB + 8u * uint32_t(m16);
+      v_rd = row + 128u * uint32_t(kq >> 1);
+      v_rd2 = row + 128u * uint32_t(1 - (kq >> 1));
+    } else {
+      v_rd = uint32_t(kq) * Geo::RB + uint32_t(m16) * Geo::VB;
+      v_rd2 = 0;
+    }
     lds_base = lds;
     p_lds = lds_addr(p);
     a_lds = lds_addr(a);
@@ -220,10 +245,15 @@ struct HeadPipe {
   __device__ void reset() {
     m_run = neg_inf();
     l_run = 0.f;
+    if constexpr (MPV) {
 #pragma unroll
-    for (int g = 0; g < GP; ++g)
+      for (int j = 0; j < NDT; ++j) o4[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    } else {
 #pragma unroll
-      for (int e = 0; e < VPL; ++e) o[g][e] = 0.f;
+      for (int g = 0; g < GP; ++g)
+#pragma unroll
+        for (int e = 0; e < VPL; ++e) o[g][e] = 0.f;
+    }
     bad = false;
   }
 
@@ -304,6 +334,11 @@ struct HeadPipe {
     l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
     m_run = m_new;
 
+    if constexpr (MPV) {
+      pv_mfma(st, t0, masked, s.t_end, pr, alpha, G);
+      return;
+    }
+
     // The probabilities move from the score layout (lane: head m16, tokens 4 kq + i) to the PV
     // layout (lane: dims of token row 4 rr + kq, all heads) through the wave's LDS slots.  These
     // accesses are inline assembly (lds_write32 / lds_read16), so the compiler does not make them
@@ -376,6 +411,56 @@ struct HeadPipe {
       }
     }
     __builtin_amdgcn_wave_barrier();
+  }
+
+  // PV on the matrix cores for the tile in stage `st` (MPV): this lane's column is query head m16
+  // and its k values are tokens 4 kq .. 4 kq + 3, so the rescale by alpha and the probabilities
+  // are lane-local.  The A operand (V^T) of tile j is dim 64 (j / 4) + 4 m16 + j % 4 of those
+  // four tokens, cut out of two 8-byte reads per token row; tokens at or past t_end read as zero
+  // (their slots may hold anything, and 0 x NaN is NaN).
+  __device__ void pv_mfma(int st, int t0, bool masked, int t_end, const float (&pr)[4], float alpha, int G) {
+    const bool rescale = __ballot(m16 < G && alpha != 1.f) != 0;
+    if (rescale) {
+#pragma unroll
+      for (int j = 0; j < NDT; ++j) o4[j] *= alpha;
+    }
+    uint32_t h01, l01, h23, l23;
+    split_pair<DT>(pr[0], pr[1], h01, l01);
+    split_pair<DT>(pr[2], pr[3], h23, l23);
+    const u32x4 pop = {h01, h23, l01, l23};
+    const uint32_t vs = lds_base + VSTAGE0 + uint32_t(st * Geo::KTILE);
+    const uint32_t a0 = vs + v_rd, a1 = vs + v_rd2;
+    u32x2 r[2][4];
+    r[0][0] = lds_read8_at<0 * Geo::RB>(a0);
+    r[0][1] = lds_read8_at<1 * Geo::RB>(a0);
+    r[0][2] = lds_read8_at<2 * Geo::RB>(a0);
+    r[0][3] = lds_read8_at<3 * Geo::RB>(a0);
+    r[1][0] = lds_read8_at<0 * Geo::RB>(a1);
+    r[1][1] = lds_read8_at<1 * Geo::RB>(a1);
+    r[1][2] = lds_read8_at<2 * Geo::RB>(a1);
+    r[1][3] = lds_read8_at<3 * Geo::RB>(a1);
+    lds_wait();
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lds_pin(r[h][i]);
+    uint32_t m01 = ~0u, m23 = ~0u;
+    if (masked) {
+      const int tb = t0 + 4 * kq;
+      m01 = (tb < t_end ? 0xffffu : 0u) | (tb + 1 < t_end ? 0xffff0000u : 0u);
+      m23 = (tb + 2 < t_end ? 0xffffu : 0u) | (tb + 3 < t_end ? 0xffff0000u : 0u);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        // element jj of the four dims read: low (jj even) or high halves of word jj / 2
+        constexpr uint32_t kSel[2] = {0x05040100u, 0x07060302u};
+        const int w = jj >> 1;
+        const uint32_t v01 = __builtin_amdgcn_perm(r[h][1][w], r[h][0][w], kSel[jj & 1]) & m01;
+        const uint32_t v23 = __builtin_amdgcn_perm(r[h][3][w], r[h][2][w], kSel[jj & 1]) & m23;
+        o4[4 * h + jj] = mfma32<DT>(u32x4{v01, v23, v01, v23}, pop, o4[4 * h + jj]);
+      }
   }
 
   // All of this wave's tiles: chunks of up to 64 tiles, DEPTH tiles in flight.
@@ -491,15 +576,24 @@ struct HeadPipe {
   // o[GP][D], then m[GP], l[GP], bad.
   __device__ void to_lds(float* ep) {
     l_run = sum_rows4(l_run);
+    if constexpr (MPV) {
+      if (m16 < GP) {
 #pragma unroll
-    for (int g = 0; g < GP; ++g)
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int e = 0; e < VPL; ++e) o[g][e] = sum_rows4(o[g][e]);
-    if (lane < 16) {
+          for (int e = 0; e < 16; ++e) ep[m16 * D + 64 * h + 16 * kq + e] = o4[4 * h + e % 4][e / 4];
+      }
+    } else {
 #pragma unroll
       for (int g = 0; g < GP; ++g)
 #pragma unroll
-        for (int e = 0; e < VPL; ++e) ep[g * D + lane * VPL + e] = o[g][e];
+        for (int e = 0; e < VPL; ++e) o[g][e] = sum_rows4(o[g][e]);
+      if (lane < 16) {
+#pragma unroll
+        for (int g = 0; g < GP; ++g)
+#pragma unroll
+          for (int e = 0; e < VPL; ++e) ep[g * D + lane * VPL + e] = o[g][e];
+      }
     }
     if (lane < GP) {
       ep[GP * D + lane] = m_run;
@@ -515,6 +609,21 @@ struct HeadPipe {
   template <class Emit>
   __device__ void finish_direct(int G, Emit emit) {
     l_run = sum_rows4(l_run);
+    if constexpr (MPV) {
+      // Lane (m16, kq) of a real head: dims 64 h + 16 kq .. + 15 of head m16.
+      if (m16 < G) {
+        const float lse = bad ? qnan() : (m_run + __builtin_amdgcn_logf(fmaf(1.f, l_run, 0.f))) * kLn2;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          float vals[16];
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            vals[e] = bad ? qnan() : fmaf(1.f, o4[4 * h + e % 4][e / 4], 0.f) / fmaf(1.f, l_run, 0.f);
+          emit(m16, 64 * h + 16 * kq, vals, lse);
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int g = 0; g < GP; ++g)
 #pragma unroll
@@ -1074,15 +1183,16 @@ __global__ __launch_bounds__(NW * 64) void step_kernel(const StepParams p) {
     const int64_t slot = int64_t(w) + b;
     if (own_heads) {
       // The wave finishes its query heads from registers, with no barrier.
-      hp.finish_direct(Gw, [&](int g, int d0, const float (&vals)[Geo::VPL], float lse) {
+      hp.finish_direct(Gw, [&](int g, int d0, const auto& vals, float lse) {
+        constexpr int N = sizeof(vals) / sizeof(float);   // contiguous dims from d0
         const int h = kvh * G + gs + g;
         if (whole) {
-          store_row<DT, Geo::VPL>(p.out, (int64_t(b) * a.hq + h) * D + d0, vals);
+          store_row<DT, N>(p.out, (int64_t(b) * a.hq + h) * D + d0, vals);
           if (d0 == 0 && p.lse_out) p.lse_out[int64_t(b) * a.hq + h] = lse;
         } else {   // device-scope stores: written through to where every XCD reads
           const BufRes row = make_bufres(&p.ws_out[(slot * a.hq + h) * D], uint32_t(D * 4));
 #pragma unroll
-          for (int c = 0; c < Geo::VPL / 4; ++c)
+          for (int c = 0; c < N / 4; ++c)
             dev_store16(row, uint32_t(d0 + 4 * c) * 4u,
                         f32x4{vals[4 * c], vals[4 * c + 1], vals[4 * c + 2], vals[4 * c + 3]});
           if (d0 == 0) dev_store(&p.ws_lse[slot * a.hq + h], lse);
