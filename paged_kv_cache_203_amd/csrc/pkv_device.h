@@ -277,6 +277,16 @@ __device__ inline u32x2 lds_read8_at(uint32_t lds_addr) {
   return r;
 }
 
+// Four 16-byte LDS reads pinned as landed while the LATER LDS operations issued after them are
+// still in flight: s_waitcnt lgkmcnt(LATER).  LDS operations of a wave complete in order, so
+// every read older than the LATER newest ones has landed (other operations counted by lgkmcnt
+// only make the wait longer).
+template <int LATER>
+__device__ inline void lds_wait_older4(u32x4 (&r)[4]) {
+  static_assert(LATER >= 0 && LATER < 16, "lgkmcnt range");
+  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]) : "i"(LATER));
+}
+
 // s_waitcnt lgkmcnt(0) for reads issued with lds_read8/16; each value read is then passed
 // through lds_pin(), which the compiler cannot move above the wait (both are volatile asm), so
 // no use of the value can be scheduled before the data has landed.

@@ -298,7 +298,14 @@ struct HeadPipe {
     u32x4 kops[NKL];
 #pragma unroll
     for (int c = 0; c < NKL; ++c) kops[c] = lds_read16(ks + rd_off[c]);
-    lds_wait_all<NKL>(kops);
+    u32x2 vr[2][4];   // MPV: the V^T operand rows, read now so that they land during QK and softmax
+    if constexpr (MPV) {
+      static_assert(NKL == 4, "head_dim 128, 16-bit");
+      pv_read(st, vr);
+      lds_wait_older4<8>(kops);
+    } else {
+      lds_wait_all<NKL>(kops);
+    }
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < NKL; ++c) {
@@ -335,7 +342,7 @@ struct HeadPipe {
     m_run = m_new;
 
     if constexpr (MPV) {
-      pv_mfma(st, t0, masked, s.t_end, pr, alpha, G);
+      pv_mfma(vr, t0, masked, s.t_end, pr, alpha, G);
       return;
     }
 
@@ -418,7 +425,23 @@ struct HeadPipe {
   // are lane-local.  The A operand (V^T) of tile j is dim 64 (j / 4) + 4 m16 + j % 4 of those
   // four tokens, cut out of two 8-byte reads per token row; tokens at or past t_end read as zero
   // (their slots may hold anything, and 0 x NaN is NaN).
-  __device__ void pv_mfma(int st, int t0, bool masked, int t_end, const float (&pr)[4], float alpha, int G) {
+  // The eight 8-byte reads of the V^T operand rows of stage `st` (MPV): dims 64 h + 4 m16 .. + 3
+  // of token rows 4 kq + i.
+  __device__ void pv_read(int st, u32x2 (&r)[2][4]) const {
+    const uint32_t vs = lds_base + VSTAGE0 + uint32_t(st * Geo::KTILE);
+    const uint32_t a0 = vs + v_rd, a1 = vs + v_rd2;
+    r[0][0] = lds_read8_at<0 * Geo::RB>(a0);
+    r[0][1] = lds_read8_at<1 * Geo::RB>(a0);
+    r[0][2] = lds_read8_at<2 * Geo::RB>(a0);
+    r[0][3] = lds_read8_at<3 * Geo::RB>(a0);
+    r[1][0] = lds_read8_at<0 * Geo::RB>(a1);
+    r[1][1] = lds_read8_at<1 * Geo::RB>(a1);
+    r[1][2] = lds_read8_at<2 * Geo::RB>(a1);
+    r[1][3] = lds_read8_at<3 * Geo::RB>(a1);
+  }
+
+  __device__ void pv_mfma(u32x2 (&r)[2][4], int t0, bool masked, int t_end, const float (&pr)[4],
+                          float alpha, int G) {
     const bool rescale = __ballot(m16 < G && alpha != 1.f) != 0;
     if (rescale) {
 #pragma unroll
@@ -428,27 +451,18 @@ struct HeadPipe {
     split_pair<DT>(pr[0], pr[1], h01, l01);
     split_pair<DT>(pr[2], pr[3], h23, l23);
     const u32x4 pop = {h01, h23, l01, l23};
-    const uint32_t vs = lds_base + VSTAGE0 + uint32_t(st * Geo::KTILE);
-    const uint32_t a0 = vs + v_rd, a1 = vs + v_rd2;
-    u32x2 r[2][4];
-    r[0][0] = lds_read8_at<0 * Geo::RB>(a0);
-    r[0][1] = lds_read8_at<1 * Geo::RB>(a0);
-    r[0][2] = lds_read8_at<2 * Geo::RB>(a0);
-    r[0][3] = lds_read8_at<3 * Geo::RB>(a0);
-    r[1][0] = lds_read8_at<0 * Geo::RB>(a1);
-    r[1][1] = lds_read8_at<1 * Geo::RB>(a1);
-    r[1][2] = lds_read8_at<2 * Geo::RB>(a1);
-    r[1][3] = lds_read8_at<3 * Geo::RB>(a1);
     lds_wait();
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int i = 0; i < 4; ++i) lds_pin(r[h][i]);
-    uint32_t m01 = ~0u, m23 = ~0u;
-    if (masked) {
-      const int tb = t0 + 4 * kq;
-      m01 = (tb < t_end ? 0xffffu : 0u) | (tb + 1 < t_end ? 0xffff0000u : 0u);
-      m23 = (tb + 2 < t_end ? 0xffffu : 0u) | (tb + 3 < t_end ? 0xffff0000u : 0u);
+    if (masked) {   // r[h][i] holds token 4 kq + i only
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t mi = t0 + 4 * kq + i < t_end ? ~0u : 0u;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) r[h][i] = u32x2{r[h][i].x & mi, r[h][i].y & mi};
+      }
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h)
@@ -457,8 +471,8 @@ struct HeadPipe {
         // element jj of the four dims read: low (jj even) or high halves of word jj / 2
         constexpr uint32_t kSel[2] = {0x05040100u, 0x07060302u};
         const int w = jj >> 1;
-        const uint32_t v01 = __builtin_amdgcn_perm(r[h][1][w], r[h][0][w], kSel[jj & 1]) & m01;
-        const uint32_t v23 = __builtin_amdgcn_perm(r[h][3][w], r[h][2][w], kSel[jj & 1]) & m23;
+        const uint32_t v01 = __builtin_amdgcn_perm(r[h][1][w], r[h][0][w], kSel[jj & 1]);
+        const uint32_t v23 = __builtin_amdgcn_perm(r[h][3][w], r[h][2][w], kSel[jj & 1]);
         o4[4 * h + jj] = mfma32<DT>(u32x4{v01, v23, v01, v23}, pop, o4[4 * h + jj]);
       }
   }
