@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace pkv {
 namespace dev {
 
@@ -266,6 +268,33 @@ __device__ inline u32x2 lds_read8(uint32_t lds_addr) {
   u32x2 r;
   asm volatile("ds_read_b64 %0, %1" : "=v"(r) : "v"(lds_addr));
   return r;
+}
+
+// Calls f(std::integral_constant<int, I>) for I = 0 .. N - 1, so that I can be a template argument.
+template <int I, int N, class F>
+__device__ inline void static_for_from(F& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for_from<I + 1, N>(f);
+  }
+}
+template <int N, class F>
+__device__ inline void static_for(F&& f) { static_for_from<0, N>(f); }
+
+// lds_read16 of lds_addr + OFF, the constant in the instruction's offset field.
+template <int OFF>
+__device__ inline u32x4 lds_read16_at(uint32_t lds_addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(lds_addr), "i"(OFF));
+  return r;
+}
+
+// lds_write32 to lds_addr + OFF, the constant in the instruction's offset field.
+template <int OFF>
+__device__ inline void lds_write32_at(uint32_t lds_addr, float v) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+  asm volatile("ds_write_b32 %0, %1 offset:%2" : : "v"(lds_addr), "v"(v), "i"(OFF));
 }
 
 // lds_read8 of lds_addr + OFF, the constant in the instruction's offset field.

@@ -286,13 +286,13 @@ __device__ inline void prefix_body(const PrefixParams& p, int id, PrefixShared<D
       const u32x4 a = t0 < wg_end ? vreg[k][0] : u32x4{0u, 0u, 0u, 0u};
       const u32x4 b = t0 + 1 < wg_end ? vreg[k][1] : u32x4{0u, 0u, 0u, 0u};
       const uint32_t col = base + uint32_t(8 * vc[k]) * VST + 4u * uint32_t(vtp[k]);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
+      static_for<4>([&](auto wc) {
+        constexpr int w = decltype(wc)::value;
         const uint32_t lo = (a[w] & 0xffffu) | (b[w] << 16);
         const uint32_t hi = (a[w] >> 16) | (b[w] & 0xffff0000u);
-        lds_write32(col + uint32_t(2 * w) * VST, __uint_as_float(lo));
-        lds_write32(col + uint32_t(2 * w + 1) * VST, __uint_as_float(hi));
-      }
+        lds_write32_at<(2 * w) * VST>(col, __uint_as_float(lo));
+        lds_write32_at<(2 * w + 1) * VST>(col, __uint_as_float(hi));
+      });
     }
   };
 
@@ -308,6 +308,13 @@ __device__ inline void prefix_body(const PrefixParams& p, int id, PrefixShared<D
 
   // A wave whose rows all end before the partition only helps load the blocks.
   const bool wave_active = __ballot(my_lim_any > t_lo) != 0;
+  // This lane's operand reads within a buffer: K slice 4 c + kq of token row m16 (swizzled), and
+  // the V^T row of dim m16 at tokens 8 kq ..; tile, dim-tile and token offsets are constants in
+  // the read instructions.
+  uint32_t krd[NKL];
+#pragma unroll
+  for (int c = 0; c < NKL; ++c) krd[c] = uint32_t(m16) * RB + uint32_t((4 * c + kq) ^ (m16 & Geo::SWZ)) * 16u;
+  const uint32_t vrd = uint32_t(m16) * VST + 8u * uint32_t(kq);
 
   auto compute = [&](int n, int bf) {
     if (!wave_active) return;
@@ -317,15 +324,16 @@ __device__ inline void prefix_body(const PrefixParams& p, int id, PrefixShared<D
 
     // ---- S^T tiles = K . Q^T -----------------------------------------------------------------
     f32x4 s[RBW][4];
+    uint32_t ka[NKL];
 #pragma unroll
-    for (int tp = 0; tp < 4; tp += 2) {
+    for (int c = 0; c < NKL; ++c) ka[c] = kb + krd[c];
+    static_for<2>([&](auto tpc) {
+      constexpr int tp = 2 * decltype(tpc)::value;   // tile pair: tiles tp, tp + 1
       u32x4 kop[2 * NKL];
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int c = 0; c < NKL; ++c)
-          kop[j * NKL + c] = lds_read16(kb + uint32_t(16 * (tp + j) + m16) * RB +
-                                        uint32_t((4 * c + kq) ^ (m16 & Geo::SWZ)) * 16u);
+      static_for<2 * NKL>([&](auto ic) {
+        constexpr int i = decltype(ic)::value, j = i / NKL, c = i % NKL;
+        kop[i] = lds_read16_at<(16 * (tp + j)) * RB>(ka[c]);
+      });
       lds_wait_all<2 * NKL>(kop);
 #pragma unroll
       for (int j = 0; j < 2; ++j)
@@ -336,7 +344,7 @@ __device__ inline void prefix_body(const PrefixParams& p, int id, PrefixShared<D
           for (int c = 0; c < NKL; ++c) acc = mfma32<DT>(kop[j * NKL + c], qop[rb][c], acc);
           s[rb][tp + j] = acc;
         }
-    }
+    });
 
     // ---- online softmax (lane: row m16 of block rb, tokens 16 tt + 4 kq + i) -----------------
     const bool need_mask = __ballot(lane_min < t0 + kTB) != 0;
@@ -348,12 +356,19 @@ __device__ inline void prefix_body(const PrefixParams& p, int id, PrefixShared<D
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float v = s[rb][tt][i] * p.scale_log2;
-          if (need_mask && t0 + 16 * tt + 4 * kq + i >= lim[rb]) v = neg_inf();
-          s[rb][tt][i] = v;
-          mx = fmaxf(mx, v);
-        }
+        for (int i = 0; i < 4; ++i) s[rb][tt][i] *= p.scale_log2;
+      if (need_mask) {   // only blocks where some row ends
+        const int lrel = lim[rb] - t0 - 4 * kq;   // token 16 tt + 4 kq + i is masked when 16 tt + i >= lrel
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (16 * tt + i >= lrel) s[rb][tt][i] = neg_inf();
+      }
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[rb][tt][i]);
       mx = max_rows4(mx);
       const float m_new = fmaxf(m_run[rb], mx);
       const float m_use = m_new == neg_inf() ? 0.f : m_new;   // nothing unmasked yet
@@ -379,8 +394,8 @@ __device__ inline void prefix_body(const PrefixParams& p, int id, PrefixShared<D
     }
 
     // ---- O^T += V^T . P, 32 tokens per MFMA k-step -------------------------------------------
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    static_for<2>([&](auto uc) {
+      constexpr int u = decltype(uc)::value;   // tokens 32 u .. 32 u + 31 of the block
       u32x4 ph[RBW], pl[RBW];
 #pragma unroll
       for (int rb = 0; rb < RBW; ++rb) {
@@ -394,12 +409,12 @@ __device__ inline void prefix_body(const PrefixParams& p, int id, PrefixShared<D
         pl[rb] = u32x4{l[0], l[1], l[2], l[3]};
       }
       u32x2 va[NDT][2];
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const uint32_t a = vb + uint32_t(16 * dt + m16) * VST + uint32_t(64 * u + 8 * kq);
-        va[dt][0] = lds_read8(a);
-        va[dt][1] = lds_read8(a + 32u);
-      }
+      const uint32_t va0 = vb + vrd;
+      static_for<NDT>([&](auto dc) {
+        constexpr int dt = decltype(dc)::value;
+        va[dt][0] = lds_read8_at<16 * dt * VST + 64 * u>(va0);
+        va[dt][1] = lds_read8_at<16 * dt * VST + 64 * u + 32>(va0);
+      });
       lds_wait();
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
@@ -415,7 +430,7 @@ __device__ inline void prefix_body(const PrefixParams& p, int id, PrefixShared<D
           o[rb][dt] = mfma32<DT>(av, pl[rb], o[rb][dt]);
         }
       }
-    }
+    });
   };
 
   issue(0, 0);
