@@ -812,10 +812,12 @@ __device__ inline int step_tiles(const StepParams& p, int b) {
 // (B + 1 entries, in LDS); the `groups` ranges cut the weighted line [0, WT) evenly, and a range
 // owns the tiles whose weighted start falls in it.  Everything depends on the lengths only.
 // The start weight was measured: three tiles with one wave per KV head (12 units: 113.5 us for
-// the Llama-3-8B-shaped step, against 115.5 us at 8 and 118 us at 4), four when several waves
-// share a head (16 units: 45.2 us for the Qwen2-7B-shaped step with its pairs of waves sharing
-// stages, against 47.3 at 8, 46.3 at 12, 45.6 at 24 and 45.9 at 32).
-__device__ inline int start_units(int waves_per_head) { return waves_per_head == 1 ? 12 : 16; }
+// the Llama-3-8B-shaped step, against 115.5 us at 8 and 118 us at 4; with PV on the matrix
+// cores 16 and 20 units measure the same), six when several waves share a head (24 units: with
+// PV on the matrix cores, 40.2 us for the Qwen2-7B-shaped step with its pairs of waves sharing
+// stages, against 41.7 at 16, and 41.1 against 41.8 on another box, where 32 and 40 gave 41.9
+// and 41.4).
+__device__ inline int start_units(int waves_per_head) { return waves_per_head == 1 ? 12 : 24; }
 
 struct StepSplit {
   const int* wpre;
