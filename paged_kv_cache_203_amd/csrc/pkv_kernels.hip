@@ -8,7 +8,8 @@
 //    load instruction reads whole rows.  In LDS, slice j of token t sits at j ^ (t & SWZ), which
 //    keeps the MFMA-layout reads below free of bank conflicts.
 //  * V rows are copied to LDS the same way (row-major; for 16-bit head_dim 128 the 16-byte chunks
-//    of rows 8..15 of a tile swap halves, which spreads the PV operand reads over all banks).
+//    of rows 4..7 and 12..15 of a tile swap halves, which spreads the PV operand reads over all
+//    banks).
 //  * S^T (16 tokens x 16 head slots) = K_tile . Q^T on MFMA: the G query heads of the GQA group
 //    (zero-padded to 16 columns) share every K row read.
 //  * Online softmax in the MFMA output layout (lane l: tokens 4(l/16)..+3 of head l % 16), base 2.
@@ -158,19 +159,20 @@ struct HeadPipe {
     for (int i = 0; i < NKL; ++i) {
       const int t_in = Geo::TPI * i + d_row;
       dma_off[i] = uint32_t(t_in) * tok_stride + uint32_t(d_pos ^ (t_in & Geo::SWZ)) * 16u;
-      // MPV: slot s of V row t holds 16-byte chunk s ^ 8 ((t >> 3) & 1), so that the PV operand
-      // reads of rows 4 kq + i take the two halves of the banks for kq < 2 and kq >= 2.
-      const int vsw = MPV ? 8 * ((t_in >> 3) & 1) : 0;
+      // MPV: slot s of V row t holds 16-byte chunk s ^ 8 ((t >> 2) & 1), so that the PV operand
+      // reads of rows 4 kq + i take the two halves of the banks for even and odd kq (lanes 0..31
+      // of an 8-byte read are served together).
+      const int vsw = MPV ? 8 * ((t_in >> 2) & 1) : 0;
       vdma_off[i] = uint32_t(t_in) * tok_stride + uint32_t(d_pos ^ vsw) * 16u;
     }
 #pragma unroll
     for (int c = 0; c < NKL; ++c)
       rd_off[c] = uint32_t(m16) * Geo::RB + uint32_t((4 * c + kq) ^ (m16 & Geo::SWZ)) * 16u;
     if constexpr (MPV) {
-      // Dims 64 h + 4 m16 .. + 3 of row 4 kq: chunk 8 h + m16 / 2 at slot 8 (h ^ (kq >> 1)) + m16 / 2.
+      // Dims 64 h + 4 m16 .. + 3 of row 4 kq: chunk 8 h + m16 / 2 at slot 8 (h ^ (kq & 1)) + m16 / 2.
       const uint32_t row = uint32_t(4 * kq) * Geo::RB + 8u * uint32_t(m16);
-      v_rd = row + 128u * uint32_t(kq >> 1);
-      v_rd2 = row + 128u * uint32_t(1 - (kq >> 1));
+      v_rd = row + 128u * uint32_t(kq & 1);
+      v_rd2 = row + 128u * uint32_t(1 - (kq & 1));
     } else {
       v_rd = uint32_t(kq) * Geo::RB + uint32_t(m16) * Geo::VB;
       v_rd2 = 0;
@@ -591,11 +593,13 @@ struct HeadPipe {
   __device__ void to_lds(float* ep) {
     l_run = sum_rows4(l_run);
     if constexpr (MPV) {
-      if (m16 < GP) {
+      if (m16 < GP) {   // dims 64 h + 16 kq + 4 q .. + 3 of head m16: 16-byte writes
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) ep[m16 * D + 64 * h + 16 * kq + e] = o4[4 * h + e % 4][e / 4];
+          for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<f32x4*>(ep + m16 * D + 64 * h + 16 * kq + 4 * q) =
+                f32x4{o4[4 * h][q], o4[4 * h + 1][q], o4[4 * h + 2][q], o4[4 * h + 3][q]};
       }
     } else {
 #pragma unroll
