@@ -52,23 +52,27 @@ int heads_per_workgroup(int hkv) {
 }
 
 // KV heads per workgroup of the balanced decode step: as many as divide both hkv and the wave
-// count, then halved while some wave would hold more than four query heads (larger groups need
-// the 8- and 16-column score tiles, whose accumulators do not fit the register budget without
-// spills); with fewer heads per workgroup, the waves that share a KV head split its query heads.
-int step_heads_per_workgroup(int hkv, int group) {
+// count, then halved while some wave would hold more than `per_wave` query heads; with fewer
+// heads per workgroup, the waves that share a KV head split its query heads.  With PV on the
+// matrix cores (16-bit K/V, head_dim 128) a wave's output tile has 16 query-head columns
+// whatever the group, so up to 16 heads per wave cost no more registers or matrix-core work
+// than 4; with PV on the VALU, 8- and 16-column accumulators do not fit the register budget
+// without spills, so the limit there is 4.
+int step_heads_per_workgroup(int hkv, int group, int per_wave) {
   const int waves = pkv::decode_waves();
   int h = heads_per_workgroup(hkv);
   while (h > 1) {
     const int wph = waves / h;
     const int gw = (group + wph - 1) / wph;
     const bool split = wph > 1 && (wph - 1) * gw < group;
-    if ((split ? gw : group) <= 4) break;
+    if ((split ? gw : group) <= per_wave) break;
     h /= 2;
   }
   return h;
 }
 int step_heads_per_workgroup(const pkv_shape& s) {
-  return step_heads_per_workgroup(s.num_kv_heads, s.num_q_heads / s.num_kv_heads);
+  const int per_wave = s.dtype != PKV_F32 && s.head_dim == 128 ? 16 : 4;
+  return step_heads_per_workgroup(s.num_kv_heads, s.num_q_heads / s.num_kv_heads, per_wave);
 }
 
 // Workgroup ranges of the balanced decode step on the current device: one 8-wave workgroup per

@@ -234,11 +234,13 @@ STEP_SHAPES = [  # (Hkv, G, D, PS, dtype, max length): one wave per KV head (Hkv
     # head sizes, fp32 with head_dim 128 (one tile in flight), pages of 16 to 256 tokens.  Waves
     # that share a KV head take turns on its tiles when some would get no query head (Hkv 2 with
     # G 1 or 3, Hkv 1 with G 4), else split its query heads: in pairs sharing LDS stages (Hkv 4),
-    # or four and eight waves each loading every tile (Hkv 2 and 1 with G 16).
+    # or four and eight waves each loading every tile (Hkv 2 and 1 with G 16).  With 16-bit K/V
+    # and head_dim 128 one wave takes all of a group of up to 16 heads (Hkv 8 with G 7 and 16);
+    # with head_dim 64 such groups are split over pairs of waves (Hkv 8 with G 16).
     (2, 1, 128, 16, "bf16", 700), (2, 3, 64, 16, "bf16", 300), (8, 2, 128, 64, "f16", 2500),
     (16, 1, 128, 16, "bf16", 1200), (8, 16, 64, 256, "f16", 1500), (4, 5, 64, 32, "f32", 900),
     (8, 2, 128, 128, "f32", 1000), (1, 4, 128, 16, "bf16", 4000), (8, 7, 128, 32, "bf16", 3000),
-    (2, 16, 128, 16, "bf16", 1500), (1, 16, 64, 32, "f16", 2000),
+    (2, 16, 128, 16, "bf16", 1500), (1, 16, 64, 32, "f16", 2000), (8, 16, 128, 16, "bf16", 900),
 ]
 
 
