@@ -12,7 +12,9 @@ made by one call of pkv_paged_decode_step (one kernel launch):
 Inputs are seeded synthetic data, resident in HBM before timing starts.  The pools rotate over
 several replicas so that no step finds the previous step's KV in the 256 MB Infinity Cache.
 
-Timing: W untimed steps, then the timed region, K steps launched back to back between two HIP
+Timing: W untimed steps (200 by default: after 10 the device had not reached its steady state,
+and the timed steps read about 2 us longer than after 200, which is what a decode loop sees),
+then the timed region, K steps launched back to back between two HIP
 events on the launch stream (their average is the step kernel's average launch duration, and the
 host clock around the same region gives the step rate), then K more steps each bracketed by its
 own event pair for the median / p10 / p90 (an event pair per launch adds a few us to each).
@@ -50,7 +52,7 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[1])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--config", type=int, default=2, help="workload index (default: 2)")
     ap.add_argument("--path", choices=["step", "split", "single", "cascade", "multiquery"],
                     default="step",
@@ -70,7 +72,7 @@ def parse():
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the per-workload sweep (every workload of the suite, its own paths)")
     ap.add_argument("--config-steps", type=int, default=50, help="timed calls per path in the sweep")
-    ap.add_argument("--config-warmup", type=int, default=5)
+    ap.add_argument("--config-warmup", type=int, default=50)
     return ap.parse_args()
 
 
