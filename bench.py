@@ -72,7 +72,7 @@ def parse():
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the per-workload sweep (every workload of the suite, its own paths)")
     ap.add_argument("--config-steps", type=int, default=50, help="timed calls per path in the sweep")
-    ap.add_argument("--config-warmup", type=int, default=50)
+    ap.add_argument("--config-warmup", type=int, default=200)
     return ap.parse_args()
 
 
