@@ -210,6 +210,33 @@ int pkv_paged_decode_multi_query(const void* q, const void* k_pool, const void* 
                                  void* out, float* lse_out, const pkv_shape* shape,
                                  void* stream);
 
+/* Multi-query paged decode through the balanced decode step: the same result as
+ * pkv_paged_decode_multi_query (T = num_query_tokens new tokens per sequence, q and out
+ * [batch, T, num_q_heads, head_dim], lse_out [batch, T, num_q_heads] float32 or NULL,
+ * context_lens[b] = L_b counting the T new tokens, whose K/V rows are already in the pages;
+ * query j attends to tokens 0 .. L_b - T + j; queries with no tokens and padding rows get
+ * out = 0, lse = -inf; rows longer than the page table can address get NaN), in one launch.
+ * The T x G query rows of a KV head are the step's query columns: the batch's tiles are split
+ * evenly over the GPU as in pkv_paged_decode_step, each tile is read once for all T queries, and
+ * each column stops at its own query's position.  The pages tile decode attention over the
+ * suffix tokens of a cached context (Infinity docs, "Short shared prefix qualification").
+ * workspace: caller-owned device memory of pkv_multi_query_step_workspace_bytes(shape, T) bytes,
+ * zero-filled once before the first call and then left as each call leaves it (as for
+ * pkv_paged_decode_step; calls that overlap on one workspace race).
+ * Requirements: dtype bf16 or f16 (else PKV_EUNSUPPORTED), T >= 1, T x (num_q_heads /
+ * num_kv_heads) <= 128, T x num_q_heads <= 1024,
+ * batch <= 4096.  A row's bits depend on the batch (as for the step); pkv_paged_decode_multi_query
+ * gives bits that depend only on the row. */
+int pkv_paged_decode_multi_query_step(const void* q, const void* k_pool, const void* v_pool,
+                                      const int32_t* page_table, const int32_t* context_lens,
+                                      int32_t num_query_tokens, float scale, void* workspace,
+                                      size_t workspace_bytes, void* out, float* lse_out,
+                                      const pkv_shape* shape, void* stream);
+
+/* Workspace bytes of pkv_paged_decode_multi_query_step for this shape and num_query_tokens on
+ * the current device; 0 for an invalid shape or num_query_tokens < 1. */
+size_t pkv_multi_query_step_workspace_bytes(const pkv_shape* shape, int32_t num_query_tokens);
+
 /* Fused rotary embedding + paged KV append for the decode step's new token.
  *
  * For every row with L = context_lens[b] >= 0 (the new token's position), in one launch:

@@ -68,6 +68,10 @@ _SIGNATURES = {
     "pkv_paged_decode_multi_query": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, ctypes.c_float,
                                                     _i32, _vp, _vp, _i32, _vp, _vp,
                                                     ctypes.POINTER(PkvShape), _vp]),
+    "pkv_paged_decode_multi_query_step": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, ctypes.c_float,
+                                                         _vp, ctypes.c_size_t, _vp, _vp,
+                                                         ctypes.POINTER(PkvShape), _vp]),
+    "pkv_multi_query_step_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(PkvShape), _i32]),
     "pkv_copy_pages": (ctypes.c_int, [_vp, _vp, _vp, _i32, ctypes.POINTER(PkvShape), _vp]),
     "pkv_read_stream": (ctypes.c_int, [_vp, ctypes.c_size_t, _vp, _vp]),
     "pkv_pages_create": (_vp, [_i32, _i32]),
@@ -357,6 +361,48 @@ def paged_decode_multi_query(q, k_pool, v_pool, page_table, context_lens, partit
         context_lens.data_ptr(), int(T), scale, int(partition_tokens), partial_out.data_ptr(),
         partial_lse.data_ptr(), int(maxp), out.data_ptr(), lse_ptr, ctypes.byref(s),
         _stream(q.device)))
+    return out
+
+
+def multi_query_step_workspace_bytes(q, k_pool, page_table) -> int:
+    """Workspace bytes paged_decode_multi_query_step needs for ``q [B, T, Hq, D]``."""
+    B, T, Hq, D = q.shape
+    NP, PS, Hkv, _ = k_pool.shape
+    s = make_shape(B, Hq, Hkv, D, PS, NP, page_table.shape[1], _dtype_code(q))
+    return int(lib.pkv_multi_query_step_workspace_bytes(ctypes.byref(s), int(T)))
+
+
+def paged_decode_multi_query_step(q, k_pool, v_pool, page_table, context_lens,
+                                  scale: Optional[float] = None, out=None, lse_out=None,
+                                  workspace=None):
+    """Causal decode of T new tokens per sequence through the balanced step (one launch; the
+    T x G query rows of a KV head are its columns): ``q [B, T, Hq, D]``, ``context_lens[b]``
+    counts the T new tokens too.  Returns ``out [B, T, Hq, D]``."""
+    torch = _torch()
+    _require(q, "q", ndim=4)
+    B, T, Hq, D = q.shape
+    s = _attention_shape(torch.empty((B, Hq, D), dtype=q.dtype, device=q.device), k_pool,
+                         v_pool, page_table, context_lens)   # shapes only
+    if out is None:
+        out = torch.empty_like(q)
+    _require(out, "out", dtype=q.dtype, ndim=4, device=q.device)
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must be [B, T, Hq, D]")
+    lse_ptr = None
+    if lse_out is not None:
+        _require(lse_out, "lse_out", dtype=torch.float32, ndim=3, device=q.device)
+        if tuple(lse_out.shape) != (B, T, Hq):
+            raise ValueError("lse_out must be [B, T, Hq]")
+        lse_ptr = lse_out.data_ptr()
+    need = int(lib.pkv_multi_query_step_workspace_bytes(ctypes.byref(s), int(T)))
+    if workspace is None:   # zero-filled once: the step leaves its counters at zero
+        workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=q.device)
+    _require(workspace, "workspace", dtype=torch.uint8, ndim=1, device=q.device)
+    scale = _default_scale(s.head_dim) if scale is None else float(scale)
+    _check(lib.pkv_paged_decode_multi_query_step(
+        q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), page_table.data_ptr(),
+        context_lens.data_ptr(), int(T), scale, workspace.data_ptr(), workspace.numel(),
+        out.data_ptr(), lse_ptr, ctypes.byref(s), _stream(q.device)))
     return out
 
 

@@ -304,19 +304,36 @@ size_t pkv_decode_step_workspace_bytes(const pkv_shape* shape) {
 }
 
 namespace {
+// The shape the step runs over: the caller's, or for the multi-query step (q_tokens = T > 1) the
+// same with T x num_q_heads heads (query token j of query head h is head (h / G) x T G + j G + h % G).
+pkv_shape step_shape(const pkv_shape& s, int32_t q_tokens) {
+  pkv_shape v = s;
+  if (q_tokens > 1) v.num_q_heads = s.num_q_heads * q_tokens;
+  return v;
+}
+
 int decode_step(const char* name, const void* q, const void* k_new, const void* v_new,
                 void* k_pool, void* v_pool, const int32_t* page_table,
                 const int32_t* context_lens, const float* rope_cos, const float* rope_sin,
                 int32_t rope_positions, float scale, void* workspace, size_t workspace_bytes,
-                void* out, float* lse_out, const pkv_shape* shape, void* stream) {
+                void* out, float* lse_out, const pkv_shape* user_shape, void* stream,
+                int32_t q_tokens = 1) {
   std::string msg;
-  int rc = pkv::check_shape(shape, msg);
+  int rc = pkv::check_shape(user_shape, msg);
   if (rc) return set_error(rc, std::string(name) + ": " + msg);
+  const pkv_shape vshape = step_shape(*user_shape, q_tokens);
+  const pkv_shape* shape = &vshape;
   const int64_t groups = shape->batch ? step_groups(*shape) : 1;
   const pkv::StepWorkspace ws =
       pkv::step_workspace(*shape, groups ? groups : 1, step_heads_per_workgroup(*shape));
-  rc = pkv::check_step(q, k_new, v_new, k_pool, v_pool, page_table, context_lens, scale, workspace,
-                       workspace_bytes, groups ? ws.bytes : 0, out, lse_out, shape, msg);
+  if (q_tokens > 1)
+    rc = pkv::check_multi_query_step(q, k_pool, v_pool, page_table, context_lens, q_tokens, scale,
+                                     workspace, workspace_bytes, groups ? ws.bytes : 0, out,
+                                     lse_out, user_shape, shape, msg);
+  else
+    rc = pkv::check_step(q, k_new, v_new, k_pool, v_pool, page_table, context_lens, scale,
+                         workspace, workspace_bytes, groups ? ws.bytes : 0, out, lse_out, shape,
+                         msg);
   if (!rc && rope_cos)
     rc = pkv::check_rope_tables(k_new, rope_cos, rope_sin, rope_positions, out, lse_out, workspace,
                                 workspace_bytes, shape, msg);
@@ -345,6 +362,7 @@ int decode_step(const char* name, const void* q, const void* k_new, const void* 
   p.rope_cos = rope_cos;
   p.rope_sin = rope_sin;
   p.rope_rows = rope_positions;
+  p.q_tokens = q_tokens;
   (void)hipGetLastError();
   return launch_status(pkv::launch_step(p, shape->dtype, shape->head_dim,
                                         group_pad(p.qsplit ? gw : p.a.group),
@@ -352,6 +370,28 @@ int decode_step(const char* name, const void* q, const void* k_new, const void* 
                        name);
 }
 }  // namespace
+
+int pkv_paged_decode_multi_query_step(const void* q, const void* k_pool, const void* v_pool,
+                                      const int32_t* page_table, const int32_t* context_lens,
+                                      int32_t num_query_tokens, float scale, void* workspace,
+                                      size_t workspace_bytes, void* out, float* lse_out,
+                                      const pkv_shape* shape, void* stream) {
+  if (num_query_tokens < 1)
+    return set_error(PKV_EINVAL, "pkv_paged_decode_multi_query_step: num_query_tokens must be >= 1");
+  return decode_step("pkv_paged_decode_multi_query_step", q, nullptr, nullptr,
+                     const_cast<void*>(k_pool), const_cast<void*>(v_pool), page_table,
+                     context_lens, nullptr, nullptr, 0, scale, workspace, workspace_bytes, out,
+                     lse_out, shape, stream, num_query_tokens);
+}
+
+size_t pkv_multi_query_step_workspace_bytes(const pkv_shape* shape, int32_t num_query_tokens) {
+  std::string msg;
+  if (pkv::check_shape(shape, msg) != PKV_OK || num_query_tokens < 1) return 0;
+  const pkv_shape v = step_shape(*shape, num_query_tokens);
+  const int64_t groups = step_groups(v);
+  if (groups == 0) return 0;
+  return size_t(pkv::step_workspace(v, groups, step_heads_per_workgroup(v)).bytes);
+}
 
 int pkv_paged_decode_step(const void* q, const void* k_new, const void* v_new, void* k_pool,
                           void* v_pool, const int32_t* page_table, const int32_t* context_lens,

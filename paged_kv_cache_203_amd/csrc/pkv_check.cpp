@@ -30,7 +30,7 @@ int elem_bytes(int32_t dtype) {
   }
 }
 
-int check_shape(const pkv_shape* s, std::string& msg) {
+int check_shape(const pkv_shape* s, std::string& msg, int max_group) {
   if (!s) return fail(msg, PKV_EINVAL, "shape is NULL");
   if (s->batch < 0) return fail(msg, PKV_EINVAL, "batch must be >= 0");
   if (s->num_q_heads <= 0 || s->num_kv_heads <= 0)
@@ -46,8 +46,10 @@ int check_shape(const pkv_shape* s, std::string& msg) {
     return fail(msg, PKV_EUNSUPPORTED, "head_dim must be 64 or 128");
   if (!is_pow2(s->page_size) || s->page_size < 16 || s->page_size > 256)
     return fail(msg, PKV_EUNSUPPORTED, "page_size must be a power of two in [16, 256]");
-  if (s->num_q_heads / s->num_kv_heads > 16)
-    return fail(msg, PKV_EUNSUPPORTED, "group size num_q_heads / num_kv_heads must be <= 16");
+  if (s->num_q_heads / s->num_kv_heads > max_group)
+    return fail(msg, PKV_EUNSUPPORTED,
+                max_group == 16 ? "group size num_q_heads / num_kv_heads must be <= 16"
+                                : "query columns per KV head (num_query_tokens x group) must be <= 128");
   // Tokens addressable by one row, and the largest in-page byte offset, must fit in int32.
   const int64_t row_tokens = int64_t(s->max_pages_per_seq) * s->page_size;
   if (row_tokens > INT32_MAX) return fail(msg, PKV_EINVAL, "max_pages_per_seq * page_size overflows int32");
@@ -308,8 +310,9 @@ StepWorkspace step_workspace(const pkv_shape& s, int64_t groups, int heads_per_w
 int check_step(const void* q, const void* k_new, const void* v_new, const void* k_pool,
                const void* v_pool, const int32_t* page_table, const int32_t* context_lens,
                float scale, const void* workspace, size_t workspace_bytes, uint64_t needed,
-               const void* out, const float* lse_out, const pkv_shape* s, std::string& msg) {
-  int rc = check_shape(s, msg);
+               const void* out, const float* lse_out, const pkv_shape* s, std::string& msg,
+               int max_group) {
+  int rc = check_shape(s, msg, max_group);
   if (rc) return rc;
   if (s->batch > kMaxStepBatch)
     return fail(msg, PKV_EUNSUPPORTED, "batch must be <= 4096 for the decode step");
@@ -357,7 +360,8 @@ int check_step(const void* q, const void* k_new, const void* v_new, const void* 
   }
   if (needed == 0) return fail(msg, PKV_ELAUNCH, "no device available to size the workspace");
   if (workspace_bytes < needed)
-    return fail(msg, PKV_EWORKSPACE, "workspace smaller than pkv_decode_step_workspace_bytes()");
+    return fail(msg, PKV_EWORKSPACE, "workspace smaller than pkv_decode_step_workspace_bytes() "
+                                      "(pkv_multi_query_step_workspace_bytes() for the multi-query step)");
   return PKV_OK;
 }
 
@@ -403,6 +407,24 @@ int check_rope_append(const void* q, const void* k_new, const void* v_new, const
       if (overlaps(ins[i], ins_n[i], ins[j], ins_n[j]))
         return fail(msg, PKV_EINVAL, "a pool overlaps q or the rotary cache");
   return PKV_OK;
+}
+
+int check_multi_query_step(const void* q, const void* k_pool, const void* v_pool,
+                           const int32_t* page_table, const int32_t* context_lens,
+                           int32_t q_tokens, float scale, const void* workspace,
+                           size_t workspace_bytes, uint64_t needed, const void* out,
+                           const float* lse_out, const pkv_shape* s, const pkv_shape* vs,
+                           std::string& msg) {
+  int rc = check_shape(s, msg);
+  if (rc) return rc;
+  if (q_tokens < 1) return fail(msg, PKV_EINVAL, "num_query_tokens must be >= 1");
+  if (s->dtype != PKV_BF16 && s->dtype != PKV_F16)
+    return fail(msg, PKV_EUNSUPPORTED, "the multi-query step supports bf16 and f16 only");
+  if (int64_t(q_tokens) * (s->num_q_heads / s->num_kv_heads) > kMaxMultiQueryColumns)
+    return fail(msg, PKV_EUNSUPPORTED,
+                "num_query_tokens * (num_q_heads / num_kv_heads) must be <= 128 for the multi-query step");
+  return check_step(q, nullptr, nullptr, k_pool, v_pool, page_table, context_lens, scale, workspace,
+                    workspace_bytes, needed, out, lse_out, vs, msg, kMaxMultiQueryColumns);
 }
 
 int check_copy_pages(const void* k_pool, const void* v_pool, const int32_t* pairs,

@@ -15,7 +15,9 @@ namespace pkv {
 int elem_bytes(int32_t dtype);
 
 // Sizes every call shares: positive heads, Hq % Hkv == 0, supported D / PS / G / dtype.
-int check_shape(const pkv_shape* s, std::string& msg);
+// max_group: the largest num_q_heads / num_kv_heads accepted (16 for the attention calls; the
+// multi-query step checks its T x Hq heads against its own limit).
+int check_shape(const pkv_shape* s, std::string& msg, int max_group = 16);
 
 // Byte extent of each tensor for a checked shape.
 struct Extents {
@@ -93,7 +95,20 @@ StepWorkspace step_workspace(const pkv_shape& s, int64_t groups, int heads_per_w
 int check_step(const void* q, const void* k_new, const void* v_new, const void* k_pool,
                const void* v_pool, const int32_t* page_table, const int32_t* context_lens,
                float scale, const void* workspace, size_t workspace_bytes, uint64_t needed,
-               const void* out, const float* lse_out, const pkv_shape* s, std::string& msg);
+               const void* out, const float* lse_out, const pkv_shape* s, std::string& msg,
+               int max_group = 16);
+
+// The multi-query step: `s` is the caller's shape; the step runs over vs (num_q_heads = T x Hq),
+// whose workspace needs `needed` bytes.
+int check_multi_query_step(const void* q, const void* k_pool, const void* v_pool,
+                           const int32_t* page_table, const int32_t* context_lens,
+                           int32_t q_tokens, float scale, const void* workspace,
+                           size_t workspace_bytes, uint64_t needed, const void* out,
+                           const float* lse_out, const pkv_shape* s, const pkv_shape* vs,
+                           std::string& msg);
+
+// Most query tokens x GQA group of the multi-query step (eight waves of 16 head columns).
+constexpr int kMaxMultiQueryColumns = 128;
 
 int check_copy_pages(const void* k_pool, const void* v_pool, const int32_t* pairs,
                      int32_t n_pairs, const pkv_shape* s, std::string& msg);

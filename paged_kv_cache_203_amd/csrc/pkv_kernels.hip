@@ -85,6 +85,9 @@ struct DecodeShared {
   float a[NW][GP] __attribute__((aligned(16)));
 };
 
+// HeadSource::causal0 when no column has a causal limit (leaves room for adding a query index).
+constexpr int kNoCausalLimit = 1 << 30;
+
 // What one wave streams: one KV head of one sequence over logical tokens [t_begin, t_end).
 struct HeadSource {
   const char* kpool;
@@ -102,6 +105,10 @@ struct HeadSource {
   const float* rope_cos;
   const float* rope_sin;
   int rope_pos;
+  // Multi-query decode: query column c of the wave attends to tokens t < causal0 + q_j (q_j: the
+  // column's query token, a HeadPipe lane constant) as well as t < t_end; a large value when
+  // every column sees the whole range.
+  int causal0 = kNoCausalLimit;
   // 1: this source's tile loads keep the default cache policy instead of the non-temporal one,
   // because another wave of the workgroup loads the same rows in the same round and should find
   // them in L2.
@@ -111,7 +118,9 @@ struct HeadSource {
   int part = 0;
 };
 
-template <int DT, int D, int GP, int DEPTH, bool ROPE = false>
+// MQ: multi-query decode through the step (per-lane q rows and causal limits, columns that may
+// see no token); the other instances compile to the plain decode code.
+template <int DT, int D, int GP, int DEPTH, bool ROPE = false, bool MQ = false>
 struct HeadPipe {
   using Geo = TileGeo<DT, D>;
   static constexpr int NKL = Geo::NKL, VPL = Geo::VPL, VW = Geo::VW;
@@ -135,6 +144,8 @@ struct HeadPipe {
   uint32_t v_rd;           // LDS offset (within a V stage) of this lane's dims of row kq
   uint32_t v_rd2;          // MPV: ... of its second group of dims (see init)
   uint32_t lds_base;       // this wave's K stages, then its V stages
+  int64_t q_off;           // MQ: byte offset of this lane's q row from the source's q_group
+  int q_j;                 // MQ: this lane's query token
   uint32_t p_lds;          // LDS address of this wave's p[16][GP]: a tile's probabilities
   uint32_t a_lds;          // LDS address of this wave's a[GP]: the tile's rescale factors
   // per-head state
@@ -154,6 +165,8 @@ struct HeadPipe {
     lane = threadIdx.x & 63;
     m16 = lane & 15;
     kq = lane >> 4;
+    q_off = int64_t(m16) * Geo::RB;
+    q_j = 0;
     const int d_row = lane / Geo::SPR, d_pos = lane % Geo::SPR;
 #pragma unroll
     for (int i = 0; i < NKL; ++i) {
@@ -185,7 +198,7 @@ struct HeadPipe {
   // Q^T operand: lane holds q[head m16][16-byte slices 4c + kq]; zero for padded heads.
   // `q_group` points at the first query head of the GQA group.
   __device__ void load_q(const char* q_group, int G) {
-    const char* qrow = q_group + int64_t(m16) * Geo::RB;
+    const char* qrow = q_group + (MQ ? q_off : int64_t(m16) * Geo::RB);
 #pragma unroll
     for (int c = 0; c < NKL; ++c)
       qreg[c] = (m16 < G) ? *reinterpret_cast<const u32x4*>(qrow + 64 * c + 16 * kq)
@@ -206,7 +219,7 @@ struct HeadPipe {
   // Start the loads of the next run()'s q operand and first page ids, so that their latency
   // overlaps the current work; the next run() on `s` then takes them instead of loading.
   __device__ void prefetch(const HeadSource& s, int G) {
-    const char* qrow = s.q_group + int64_t(m16) * Geo::RB;
+    const char* qrow = s.q_group + (MQ ? q_off : int64_t(m16) * Geo::RB);
 #pragma unroll
     for (int c = 0; c < NKL; ++c)
       q_pref[c] = (m16 < G) ? *reinterpret_cast<const u32x4*>(qrow + 64 * c + 16 * kq)
@@ -293,7 +306,7 @@ struct HeadPipe {
   // Attend to the tile held in stage `st` (its loads have completed).
   __device__ void process(const HeadSource& s, int st, int tile, float scale_log2, int G) {
     const int t0 = s.t_begin + tile * kTile;
-    const bool masked = t0 + kTile > s.t_end;
+    const bool masked = t0 + kTile > (MQ ? min(s.t_end, s.causal0) : s.t_end);
     const uint32_t ks = lds_base + uint32_t(st * Geo::KTILE);
 
     // ---- S^T = K . Q^T ---------------------------------------------------------------------
@@ -332,14 +345,16 @@ struct HeadPipe {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       sc[i] = acc[i] * scale_log2;
-      if (masked && t0 + 4 * kq + i >= s.t_end) sc[i] = neg_inf();
+      if (masked && t0 + 4 * kq + i >= (MQ ? min(s.t_end, s.causal0 + q_j) : s.t_end)) sc[i] = neg_inf();
     }
     const float mx = max_rows4(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
     const float m_new = fmaxf(m_run, mx);
-    const float alpha = fast_exp2(m_run - m_new);
+    // MQ: a column may have seen no token yet (its maximum is then -inf)
+    const float m_use = MQ && m_new == neg_inf() ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
     float pr[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(sc[i] - m_new);
+    for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(sc[i] - m_use);
     l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
     m_run = m_new;
 
@@ -630,13 +645,14 @@ struct HeadPipe {
     if constexpr (MPV) {
       // Lane (m16, kq) of a real head: dims 64 h + 16 kq .. + 15 of head m16.
       if (m16 < G) {
+        // MQ, l = 0: a column with no token in this range (output 0, lse -inf)
         const float lse = bad ? qnan() : (m_run + __builtin_amdgcn_logf(fmaf(1.f, l_run, 0.f))) * kLn2;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           float vals[16];
 #pragma unroll
           for (int e = 0; e < 16; ++e)
-            vals[e] = bad ? qnan() : fmaf(1.f, o4[4 * h + e % 4][e / 4], 0.f) / fmaf(1.f, l_run, 0.f);
+            vals[e] = bad ? qnan() : MQ && !(l_run > 0.f) ? 0.f : fmaf(1.f, o4[4 * h + e % 4][e / 4], 0.f) / fmaf(1.f, l_run, 0.f);
           emit(m16, 64 * h + 16 * kq, vals, lse);
         }
       }
@@ -653,7 +669,7 @@ struct HeadPipe {
       const float mg = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m_run), g));
       float vals[VPL];
 #pragma unroll
-      for (int e = 0; e < VPL; ++e) vals[e] = bad ? qnan() : fmaf(1.f, o[g][e], 0.f) / fmaf(1.f, lg, 0.f);
+      for (int e = 0; e < VPL; ++e) vals[e] = bad ? qnan() : MQ && !(lg > 0.f) ? 0.f : fmaf(1.f, o[g][e], 0.f) / fmaf(1.f, lg, 0.f);
       const float lse = bad ? qnan() : (mg + __builtin_amdgcn_logf(fmaf(1.f, lg, 0.f))) * kLn2;
       if (lane < 16) emit(g, lane * VPL, vals, lse);
     }
@@ -661,8 +677,9 @@ struct HeadPipe {
 };
 
 // Combine the waves that served one head (waves h_in, h_in + hpw, ...) and hand each output
-// element to `emit(h_in, g, d, value, lse, nan)`: value = o / l, lse in natural log.
-template <int D, int GP, int WREG, class Emit>
+// element to `emit(h_in, g, d, value, lse, nan)`: value = o / l, lse in natural log.  EMPTY_OK:
+// a column may have no token in any wave (multi-query decode): value 0, lse -inf.
+template <int D, int GP, int WREG, bool EMPTY_OK, class Emit>
 __device__ void combine_waves(const char* w_lds, int hpw, int wph, int G, int nthreads, Emit emit) {
   for (int idx = threadIdx.x; idx < hpw * G * D; idx += nthreads) {
     const int h_in = idx / (G * D);
@@ -675,16 +692,18 @@ __device__ void combine_waves(const char* w_lds, int hpw, int wph, int G, int nt
       M = fmaxf(M, e[GP * D + g]);
       any_bad += e[GP * D + 2 * GP];
     }
+    const float Mu = EMPTY_OK && M == neg_inf() ? 0.f : M;
     float lsum = 0.f, osum = 0.f;
     for (int k = 0; k < wph; ++k) {
       const float* e = reinterpret_cast<const float*>(w_lds + (h_in + k * hpw) * WREG);
-      const float sc = fast_exp2(e[GP * D + g] - M);
+      const float sc = fast_exp2(e[GP * D + g] - Mu);
       lsum = fmaf(sc, e[GP * D + GP + g], lsum);
       osum = fmaf(sc, e[g * D + d], osum);
     }
     const bool nan_out = any_bad != 0.f;
-    emit(h_in, g, d, nan_out ? qnan() : osum / lsum,
-         nan_out ? qnan() : (M + __builtin_amdgcn_logf(lsum)) * kLn2, nan_out);
+    const bool empty = EMPTY_OK && !(lsum > 0.f);
+    emit(h_in, g, d, nan_out ? qnan() : empty ? 0.f : osum / lsum,
+         nan_out ? qnan() : empty ? neg_inf() : (M + __builtin_amdgcn_logf(lsum)) * kLn2, nan_out);
   }
 }
 
@@ -755,7 +774,7 @@ __device__ inline void decode_body(const DecodeParams& p, int id,
   hp.to_lds(reinterpret_cast<float*>(sm.w[wave]));
   __syncthreads();
 
-  combine_waves<D, GP, Shm::WREG>(&sm.w[0][0], HPW, WPH, G, NW * 64,
+  combine_waves<D, GP, Shm::WREG, false>(&sm.w[0][0], HPW, WPH, G, NW * 64,
       [&](int h_in, int g, int d, float val, float lse, bool) {
         const int h = (hg * HPW + h_in) * G + g;
         if constexpr (PARTIAL) {
@@ -885,6 +904,17 @@ struct StepSplit {
   }
 };
 
+// Row (in head_dim rows) of q, out and lse_out for sequence b and head h of the step.  The
+// multi-query step (q_tokens = T > 1) runs over T x Hq heads: head kvh * G + c (G = T x the GQA
+// group QG) is query token c / QG of query head kvh * QG + c % QG, whose rows are [b, T, Hq].
+__device__ inline int64_t step_row(const StepParams& p, int b, int h) {
+  const int T = p.q_tokens;
+  if (T <= 1) return int64_t(b) * p.a.hq + h;
+  const int G = p.a.group, QG = G / T, HQ = p.a.hq / T;
+  const int kvh = h / G, c = h - kvh * G;
+  return (int64_t(b) * T + c / QG) * HQ + int64_t(kvh) * QG + c % QG;
+}
+
 // A piece of `tiles` tiles arrives on its sequence's counter (pkv_arrival.h): the word is first
 // raised to this call's floor, so that a count an earlier call left behind starts again from zero,
 // then the tiles are added.  Returns the tiles this call had counted before.
@@ -940,7 +970,7 @@ __device__ void weight_prefix(const StepParams& p, int su, int* wpre, uint8_t* t
 // carrying a running maximum from one group of pieces to the next.
 // `flags` (NT ints of LDS) receives which of the first NT candidate ranges hold a piece; all
 // threads of the block take part.
-template <int DT, int D, int NT>
+template <int DT, int D, int NT, bool MQ>
 __device__ void step_merge(const StepParams& p, const StepSplit& sp, int b, int hg, int NH, int S,
                            int E, int* flags) {
   constexpr int kMU = 8, kCols = 2;
@@ -992,13 +1022,14 @@ __device__ void step_merge(const StepParams& p, const StepSplit& sp, int b, int 
         float mc = m[k];
 #pragma unroll
         for (int u = 0; u < kMU; ++u) mc = fmaxf(mc, ls[k][u]);
-        const float r = fast_exp2((m[k] - mc) * kLog2e);
+        const float mu = MQ && mc == neg_inf() ? 0.f : mc;   // MQ: no piece saw a token of the column
+        const float r = fast_exp2((m[k] - mu) * kLog2e);
         l[k] *= r;
 #pragma unroll
         for (int j = 0; j < 4; ++j) o[k][j] *= r;
 #pragma unroll
         for (int u = 0; u < kMU; ++u) {
-          const float wt = fast_exp2((ls[k][u] - mc) * kLog2e);
+          const float wt = fast_exp2((ls[k][u] - mu) * kLog2e);
           l[k] += wt;
 #pragma unroll
           for (int j = 0; j < 4; ++j) o[k][j] = fmaf(wt, vs[k][u][j], o[k][j]);
@@ -1010,17 +1041,19 @@ __device__ void step_merge(const StepParams& p, const StepSplit& sp, int b, int 
     for (int k = 0; k < kCols; ++k) {
       const int c = c0 + k * NT;
       if (c >= ncol) continue;
-      const int64_t base = (int64_t(b) * a.hq + h[k]) * D + d0[k];
+      const int64_t row = MQ ? step_row(p, b, h[k]) : int64_t(b) * a.hq + h[k];
+      const int64_t base = row * D + d0[k];
+      const bool empty = MQ && !(l[k] > 0.f);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) store_elem<DT>(p.out, base + j, o[k][j] / l[k]);
+      for (int j = 0; j < 4; ++j) store_elem<DT>(p.out, base + j, empty ? 0.f : o[k][j] / l[k]);
       if (d0[k] == 0 && p.lse_out)
-        p.lse_out[int64_t(b) * a.hq + h[k]] = m[k] + __builtin_amdgcn_logf(l[k]) * kLn2;
+        p.lse_out[row] = empty ? neg_inf() : m[k] + __builtin_amdgcn_logf(l[k]) * kLn2;
     }
   }
   __syncthreads();   // `flags` may be rewritten next
 }
 
-template <int DT, int D, int GP, int NW, int DEPTH, bool ROPE>
+template <int DT, int D, int GP, int NW, int DEPTH, bool ROPE, bool MQ = false>
 __global__ __launch_bounds__(NW * 64) void step_kernel(const StepParams p) {
   using Geo = TileGeo<DT, D>;
   using Shm = DecodeShared<DT, D, GP, NW, DEPTH>;
@@ -1077,8 +1110,15 @@ __global__ __launch_bounds__(NW * 64) void step_kernel(const StepParams p) {
 
   int b = sp.seq_of_tile(lo);   // the sequence holding tile `lo`
 
-  HeadPipe<DT, D, GP, DEPTH, ROPE> hp;
+  HeadPipe<DT, D, GP, DEPTH, ROPE, MQ> hp;
   hp.init(a.tok_stride, lds_addr(sm.w[part ? wave % HPW : wave]), &sm.p[wave][0][0], &sm.a[wave][0]);
+  if constexpr (MQ) {
+    // This lane's q row within the KV head's rows ([b, T, Hq]), from its column gs + m16.
+    const int c = gs + (threadIdx.x & 15);
+    const int QG = G / p.q_tokens, HQ = a.hq / p.q_tokens;
+    hp.q_off = (int64_t(c / QG) * HQ + c % QG) * Geo::RB;
+    hp.q_j = c / QG;
+  }
 
   // This wave's source for sequence bb: the tiles of bb in this range, for its KV head.
   auto source = [&](int bb) {
@@ -1101,10 +1141,12 @@ __global__ __launch_bounds__(NW * 64) void step_kernel(const StepParams p) {
     src.stride = qsplit ? 1 : WPH;
     src.keep = qsplit && !part ? 1 : 0;
     src.part = part;   // the waves that split the head's query heads load its tiles alike
-    src.q_group = static_cast<const char*>(a.q) + (int64_t(bb) * a.hq + int64_t(kvh) * G + gs) * Geo::RB;
+    src.q_group = static_cast<const char*>(a.q) +
+                  (MQ ? step_row(p, bb, kvh * G) : int64_t(bb) * a.hq + int64_t(kvh) * G + gs) * Geo::RB;
     src.rope_cos = p.rope_cos;
     src.rope_sin = p.rope_sin;
     src.rope_pos = -1;
+    if constexpr (MQ) src.causal0 = (n_bb - 1) * kTile + ltail[bb] - p.q_tokens + 1;
     if constexpr (ROPE) {
       const int L = (n_bb - 1) * kTile + ltail[bb] - 1;   // the new token's position
       src.rope_pos = L >= 0 && L < p.rope_rows ? L : -1;
@@ -1207,8 +1249,9 @@ __global__ __launch_bounds__(NW * 64) void step_kernel(const StepParams p) {
         constexpr int N = sizeof(vals) / sizeof(float);   // contiguous dims from d0
         const int h = kvh * G + gs + g;
         if (whole) {
-          store_row<DT, N>(p.out, (int64_t(b) * a.hq + h) * D + d0, vals);
-          if (d0 == 0 && p.lse_out) p.lse_out[int64_t(b) * a.hq + h] = lse;
+          const int64_t row = MQ ? step_row(p, b, h) : int64_t(b) * a.hq + h;
+          store_row<DT, N>(p.out, row * D + d0, vals);
+          if (d0 == 0 && p.lse_out) p.lse_out[row] = lse;
         } else {   // device-scope stores: written through to where every XCD reads
           const BufRes row = make_bufres(&p.ws_out[(slot * a.hq + h) * D], uint32_t(D * 4));
 #pragma unroll
@@ -1221,12 +1264,13 @@ __global__ __launch_bounds__(NW * 64) void step_kernel(const StepParams p) {
     } else {
       hp.to_lds(reinterpret_cast<float*>(sm.w[wave]));
       __syncthreads();
-      combine_waves<D, GP, Shm::WREG>(&sm.w[0][0], HPW, WPH, G, NW * 64,
+      combine_waves<D, GP, Shm::WREG, MQ>(&sm.w[0][0], HPW, WPH, G, NW * 64,
           [&](int h_in, int g, int d, float val, float lse, bool) {
             const int h = (hg * HPW + h_in) * G + g;
             if (whole) {
-              store_elem<DT>(p.out, (int64_t(b) * a.hq + h) * D + d, val);
-              if (d == 0 && p.lse_out) p.lse_out[int64_t(b) * a.hq + h] = lse;
+              const int64_t row = MQ ? step_row(p, b, h) : int64_t(b) * a.hq + h;
+              store_elem<DT>(p.out, row * D + d, val);
+              if (d == 0 && p.lse_out) p.lse_out[row] = lse;
             } else {
               dev_store(&p.ws_out[(slot * a.hq + h) * D + d], val);
               if (d == 0) dev_store(&p.ws_lse[slot * a.hq + h], lse);
@@ -1287,7 +1331,7 @@ __global__ __launch_bounds__(NW * 64) void step_kernel(const StepParams p) {
   for (int i = 0; i < 2; ++i) {
     const int sb = i == 0 ? split_first : split_last;
     if (!merging[i]) continue;
-    step_merge<DT, D, NW * 64>(p, sp, sb, hg, HPW * a.group, prefix(sb), prefix(sb + 1), scan);
+    step_merge<DT, D, NW * 64, MQ>(p, sp, sb, hg, HPW * a.group, prefix(sb), prefix(sb + 1), scan);
     if (threadIdx.x == 0)   // ready for the next call
       __hip_atomic_store(&p.ws_count[int64_t(sb) * nhg + hg], uint64_t(0), __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
@@ -1458,6 +1502,15 @@ hipError_t launch_step_t(const StepParams& p, hipStream_t stream) {
     hipLaunchKernelGGL((step_kernel<DT, D, GP, kWaves, pipe_depth<DT, D>(), true>), dim3(unsigned(p.groups * nhg)),
                        dim3(kWaves * 64), 0, stream, p);
     return hipGetLastError();
+  }
+  if (p.q_tokens > 1) {
+    if constexpr (DT == DT_F32) {
+      return hipErrorInvalidValue;   // the multi-query step takes 16-bit types only
+    } else {
+      hipLaunchKernelGGL((step_kernel<DT, D, GP, kWaves, pipe_depth<DT, D>(), false, true>),
+                         dim3(unsigned(p.groups * nhg)), dim3(kWaves * 64), 0, stream, p);
+      return hipGetLastError();
+    }
   }
   hipLaunchKernelGGL((step_kernel<DT, D, GP, kWaves, pipe_depth<DT, D>(), false>), dim3(unsigned(p.groups * nhg)),
                      dim3(kWaves * 64), 0, stream, p);

@@ -56,6 +56,11 @@ struct StepParams {
   const float* rope_cos; // null: no rotation
   const float* rope_sin;
   int32_t rope_rows;
+  // Multi-query decode (q_tokens = T > 1, no append, no rotation): the step runs over T x Hq
+  // heads (a.hq = T x Hq, a.group = T x the GQA group); head kvh * a.group + c is query token
+  // c / (a.group / T) of query head kvh * (a.group / T) + c % (a.group / T), attending to tokens
+  // t <= L - T + (its query token); q, out, lse_out are [batch, T, Hq].  0 or 1: the decode step.
+  int32_t q_tokens;
 };
 
 struct MergeParams {

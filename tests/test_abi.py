@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 31, names
+    assert len(names) == 33, names
     for n in names:
         assert hasattr(L.lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True, text=True).stdout
@@ -185,6 +185,25 @@ def test_multi_query_rejections(L):
     assert mq(po=FAKE + 0x300000) == -1           # partials overlap the page table
     assert mq(sh=shape(L, batch=0)) == 0
     assert L.last_error().startswith("pkv_paged_decode_multi_query")
+
+
+def test_multi_query_step_rejections(L):
+    s = shape(L)   # group 4: up to 32 query tokens
+    def mq(T=4, ws=FAKE + 0x900000, wsb=1 << 30, out=FAKE + 0x500000, sh=s):
+        return L.lib.pkv_paged_decode_multi_query_step(
+            FAKE, FAKE + 0x100000, FAKE + 0x200000, FAKE + 0x300000, FAKE + 0x400000, T, 0.1,
+            ws, wsb, out, None, ctypes.byref(sh), None)
+    assert mq(T=0) == -1
+    assert mq(T=33) == -2                         # 33 x 4 query columns per KV head > 128
+    assert mq(sh=shape(L, dtype=0)) == -2         # f32: 16-bit types only
+    assert mq(ws=0) == -1
+    assert mq(out=FAKE + 0x10) == -1              # out overlaps q ([B, T, Hq, D] = 16 KB)
+    assert mq(sh=shape(L, batch=5000)) == -2      # batch above the step's limit
+    assert mq(sh=shape(L, batch=0)) == 0
+    assert L.last_error().startswith("pkv_paged_decode_multi_query_step")
+    bad = L.make_shape(1, 3, 2, 128, 16, 1, 1, 1)
+    assert L.lib.pkv_multi_query_step_workspace_bytes(ctypes.byref(bad), 4) == 0
+    assert L.lib.pkv_multi_query_step_workspace_bytes(ctypes.byref(s), 0) == 0
 
 
 def test_workspace_bytes(L):
