@@ -54,11 +54,14 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--config", type=int, default=2, help="workload index (default: 2)")
-    ap.add_argument("--path", choices=["step", "split", "single", "cascade", "multiquery"],
+    ap.add_argument("--path", choices=["step", "split", "single", "cascade", "multiquery",
+                                       "multiquery-step"],
                     default="step",
                     help="cascade: shared-prefix decode (prefix-shared workloads only); "
-                         "multiquery: --q-tokens new tokens per sequence, causal")
-    ap.add_argument("--q-tokens", type=int, default=8, help="multiquery: query tokens per sequence")
+                         "multiquery: --q-tokens new tokens per sequence, causal, over fixed "
+                         "partitions; multiquery-step: the same through the balanced step")
+    ap.add_argument("--q-tokens", type=int, default=8,
+                    help="multiquery paths: query tokens per sequence")
     ap.add_argument("--partition-tokens", type=int, default=None)
     ap.add_argument("--rope", action="store_true",
                     help="step path: rotate the new key and the query in the same launch "
@@ -106,6 +109,11 @@ def step_bytes(w, partition_tokens, path):
         qo = B * T * Hq * D * e
         kernel = kv + qo + table + partials             # partition launch
         step = kv + 2 * qo + table + 2 * partials + B * 4   # no append in this step
+        return dict(kv=kv, step=step, kernel=kernel)
+    elif path == "multiquery-step":
+        # One launch: K and V once per sequence for all its query tokens, q and out per token.
+        qo = B * w.q_tokens * Hq * D * e
+        kernel = step = kv + 2 * qo + table
         return dict(kv=kv, step=step, kernel=kernel)
     elif path == "cascade":
         # The shared prefix pages are read once: unique KV bytes, plus every partition's partial
@@ -506,7 +514,9 @@ def main():
     t_gen = time.perf_counter()
     w = W.make_workload(cfg)
     B, Hq, Hkv, D, PS = cfg.batch, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.page_size
-    w.q_tokens = args.q_tokens if args.path == "multiquery" else 1
+    mq = args.path in ("multiquery", "multiquery-step")
+    one_launch = args.path in ("step", "multiquery-step")
+    w.q_tokens = args.q_tokens if mq else 1
     if args.path == "cascade" and cfg.lengths[0] != "prefix":
         raise SystemExit("--path cascade needs a prefix-shared workload")
     P = args.partition_tokens or {"cascade": 256, "multiquery": 1024}.get(args.path) or \
@@ -520,7 +530,7 @@ def main():
     q, table, lens, alens, kn, vn, out = pr.q, pr.table, pr.lens, pr.alens, pr.kn, pr.vn, pr.out
     pools, R = pr.pools, pr.R
     maxp = pkv.partitions_needed(PS, w.page_table.shape[1], P)
-    if args.path == "multiquery":
+    if mq:
         T = args.q_tokens
         qm = to_device(fill_normal((B, T, Hq, D), cfg.dtype, w.seed, 9), cfg.dtype, dev)
         outm = torch.empty_like(qm)
@@ -543,6 +553,9 @@ def main():
     ws = None
     if args.path == "step":
         ws = torch.zeros(pkv.decode_step_workspace_bytes(q, pools[0][0], table), dtype=torch.uint8, device=dev)
+    elif args.path == "multiquery-step":
+        ws = torch.zeros(pkv.multi_query_step_workspace_bytes(qm, pools[0][0], table), dtype=torch.uint8,
+                         device=dev)
 
     def step(i, ev=None):
         """One step; with `ev`, the event pair brackets the dominant kernel only."""
@@ -550,6 +563,9 @@ def main():
         if args.path == "step":
             pkv.paged_decode_step(q, kp, vp, table, alens, scale, k_new=kn, v_new=vn, out=out,
                                   workspace=ws, **rope)
+            return
+        if args.path == "multiquery-step":
+            pkv.paged_decode_multi_query_step(qm, kp, vp, table, lens, scale, out=outm, workspace=ws)
             return
         if args.path != "multiquery":   # the multi-query rows' K/V are already in the pages
             pkv.paged_kv_append(kn, vn, kp, vp, table, alens)
@@ -595,7 +611,7 @@ def main():
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(K)]
     for i in range(K):
-        if args.path == "step":
+        if one_launch:
             evs[i][0].record(stream)
             step(args.warmup + K + i)
             evs[i][1].record(stream)
@@ -607,9 +623,9 @@ def main():
     nb = step_bytes(w, P, args.path)
     ms_step = wall * 1e3 / K
     gbs = nb["step"] / (ms_step * 1e-3) / 1e9
-    # One launch per step on the step path: the region's average is the kernel's average launch
+    # One launch per step on the step paths: the region's average is the kernel's average launch
     # duration in a back-to-back stream.  Other paths time their dominant kernel alone.
-    k_avg_us = region_us if args.path == "step" else float(kernel_us.mean())
+    k_avg_us = region_us if one_launch else float(kernel_us.mean())
     k_gbs = nb["kernel"] / (k_avg_us * 1e-6) / 1e9
     log(f"{K} steps in {wall * 1e3:.2f} ms: {ms_step * 1e3:.1f} us/step, {gbs:.0f} GB/s step; "
         f"events over the region {region_us:.1f} us/step; dominant kernel {k_avg_us:.1f} us avg, "
@@ -636,6 +652,7 @@ def main():
     kernel_name = {"split": "decode_kernel (split-KV partial attention)",
                    "cascade": "pkv_paged_decode_cascade (prefix on MFMA + suffix partitions + merge)",
                    "multiquery": "pkv_paged_decode_multi_query (partitions on MFMA + merge)",
+                   "multiquery-step": "step_kernel (pkv_paged_decode_multi_query_step: balanced attention + merge)",
                    "single": "decode_kernel (single pass)",
                    "step": "step_kernel (pkv_paged_decode_step: append + balanced attention + merge)"}[args.path]
     traffic = measured_traffic(cfg.name) if args.path == "step" and not args.rope else None
@@ -657,6 +674,7 @@ def main():
             "description": {"split": "append + split-KV paged decode attention + LSE merge",
                             "cascade": "append + shared-prefix decode: prefix on the matrix cores, suffix partitions, LSE merge",
                             "multiquery": "causal decode of q_tokens new tokens per sequence (their K/V already paged) on the matrix cores + LSE merge",
+                            "multiquery-step": "causal decode of q_tokens new tokens per sequence (their K/V already paged) in one launch: balanced split-KV attention, LSE merge",
                             "single": "append + single-pass paged decode attention",
                             "step": "one decode step in one launch: append, balanced split-KV attention, LSE merge"}[args.path],
             "batch": B, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D, "page_size": PS,
@@ -684,7 +702,7 @@ def main():
             "bytes_per_launch": nb["kernel"],
             "avg_launch_us": round(k_avg_us, 3),
             "timing": ("events on the launch stream around the K back-to-back steps of the timed "
-                       "region, divided by K" if args.path == "step" else
+                       "region, divided by K" if one_launch else
                        "an event pair around the dominant kernel of each step, averaged"),
             "median_bracketed_us": round(float(np.median(kernel_us)), 3),
             "p10_bracketed_us": round(float(np.percentile(kernel_us, 10)), 3),
