@@ -12,9 +12,12 @@ made by one call of pkv_paged_decode_step (one kernel launch):
 Inputs are seeded synthetic data, resident in HBM before timing starts.  The pools rotate over
 several replicas so that no step finds the previous step's KV in the 256 MB Infinity Cache.
 
-Timing: W untimed steps (200 by default: after 10 the device had not reached its steady state,
-and the timed steps read about 2 us longer than after 200, which is what a decode loop sees),
-then the timed region, K steps launched back to back between two HIP
+Timing: first a settle phase, untimed and reported on its own (`settle` in the line): real steps
+until --settle-ms of host time (200 ms by default) have passed, because the device needs some tens
+of milliseconds of continuous work to reach its steady clock and power state (after 10 steps the
+timed steps read about 2 us longer than after 200, on the same box; a decode loop runs in the
+steady state).  Then W untimed warmup steps (200 by default), then the timed region, K steps
+launched back to back between two HIP
 events on the launch stream (their average is the step kernel's average launch duration, and the
 host clock around the same region gives the step rate), then K more steps each bracketed by its
 own event pair for the median / p10 / p90 (an event pair per launch adds a few us to each).
@@ -53,6 +56,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--settle-ms", type=float, default=200.0,
+                    help="untimed steps before the warmup, for at least this much host time, so "
+                         "that the device reaches its steady clock state (0 disables)")
     ap.add_argument("--config", type=int, default=2, help="workload index (default: 2)")
     ap.add_argument("--path", choices=["step", "split", "single", "cascade", "multiquery",
                                        "multiquery-step"],
@@ -591,6 +597,14 @@ def main():
             if ev is not None:
                 ev[1].record(stream)
 
+    # ---- settle (reported apart from the warmup), then the W warmup steps ----
+    settle_steps, t_settle = 0, time.perf_counter()
+    while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
+        for i in range(20):
+            step(settle_steps + i)
+        settle_steps += 20
+        torch.cuda.synchronize()
+    settle_ms = (time.perf_counter() - t_settle) * 1e3
     # ---- the timed region: K steps back to back between two events on the launch stream ----
     for i in range(args.warmup):
         step(i)
@@ -663,6 +677,9 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
+        "settle": {"steps": settle_steps, "ms": round(settle_ms, 1),
+                   "what": "untimed full steps run before the warmup steps, until the device reaches "
+                           "its steady clock state (--settle-ms)"},
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
