@@ -1003,9 +1003,8 @@ __device__ void step_merge(const StepParams& p, const StepSplit& sp, int b, int 
 #pragma unroll
       for (int j = 0; j < 4; ++j) o[k][j] = 0.f;
     }
-    for (int k0 = 0; k0 < npc; k0 += kMU) {
-      float ls[kCols][kMU];
-      f32x4 vs[kCols][kMU];
+    // Pieces k0 .. k0 + kMU - 1: their log-sum-exps and rows, in flight together.
+    auto load_round = [&](int k0, float (&ls)[kCols][kMU], f32x4 (&vs)[kCols][kMU]) {
 #pragma unroll
       for (int u = 0; u < kMU; ++u) {
         const int k = k0 + u;
@@ -1017,6 +1016,9 @@ __device__ void step_merge(const StepParams& p, const StepSplit& sp, int b, int 
           vs[k][u] = ok ? dev_load16(rows, uint32_t(row * D + d0[k]) * 4) : f32x4{0.f, 0.f, 0.f, 0.f};
         }
       }
+    };
+    // Fold one round into the running (m, l, o), pieces in order.
+    auto combine = [&](const float (&ls)[kCols][kMU], const f32x4 (&vs)[kCols][kMU]) {
 #pragma unroll
       for (int k = 0; k < kCols; ++k) {
         float mc = m[k];
@@ -1036,6 +1038,24 @@ __device__ void step_merge(const StepParams& p, const StepSplit& sp, int b, int 
         }
         m[k] = mc;
       }
+    };
+    // Two register sets: the next round's loads are issued before the current round is folded,
+    // so a sequence cut into many pieces pays about one round trip, not one per round.  The fold
+    // order (and so every bit of the result) is that of one round after the other.
+    float lsA[kCols][kMU], lsB[kCols][kMU];
+    f32x4 vsA[kCols][kMU], vsB[kCols][kMU];
+    load_round(0, lsA, vsA);
+    for (int k0 = 0;;) {
+      const bool more_b = k0 + kMU < npc;
+      if (more_b) load_round(k0 + kMU, lsB, vsB);
+      combine(lsA, vsA);
+      k0 += kMU;
+      if (!more_b) break;
+      const bool more_a = k0 + kMU < npc;
+      if (more_a) load_round(k0 + kMU, lsA, vsA);
+      combine(lsB, vsB);
+      k0 += kMU;
+      if (!more_a) break;
     }
 #pragma unroll
     for (int k = 0; k < kCols; ++k) {
