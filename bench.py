@@ -291,13 +291,19 @@ def cpu_baseline(w, extra_new, seconds):
             "blas_threads_per_call": 1, **info}
 
 
-def timed(fn, K, W, stream):
-    """Run fn(i) W times untimed, then K times back to back between two events on `stream`
-    (the timed region), then K more times with an event pair around each call (the spread).
-    Returns the per-call averages of the region (events and host wall clock) and the median,
-    p10 and p90 of the individually bracketed calls."""
+def timed(fn, K, W, stream, settle_ms=0.0):
+    """Run fn(i) untimed for at least `settle_ms` of host time (the device's steady state) and
+    then W more times, then K times back to back between two events on `stream` (the timed
+    region), then K more times with an event pair around each call (the spread).  Returns the
+    per-call averages of the region (events and host wall clock) and the median, p10 and p90 of
+    the individually bracketed calls."""
     import numpy as np
     import torch
+    t_settle = time.perf_counter()
+    while (time.perf_counter() - t_settle) * 1e3 < settle_ms:
+        for i in range(20):
+            fn(i)
+        torch.cuda.synchronize()
     for i in range(W):
         fn(i)
     torch.cuda.synchronize()
@@ -370,11 +376,12 @@ class Prepared:
         self.pools = None
 
 
-def config_sweep(pkv, dev, stream, read_gbs, K, W, cpu_seconds):
+def config_sweep(pkv, dev, stream, read_gbs, K, W, cpu_seconds, settle_ms):
     """Every workload of the suite on its own paths: median / p10 / p90 per call, algorithmic
     GB/s, % of 8 TB/s and of this run's read-stream ceiling, decode tokens/s; pools rotated (and,
     where the KV fits in the Infinity Cache, also the same buffers every call); the fp64 oracle
-    timed once per workload on the host."""
+    timed once per workload on the host.  Each path settles (--settle-ms) and warms up before its
+    timed region, as the headline does."""
     import numpy as np
     import torch
     import oracle as O
@@ -395,7 +402,7 @@ def config_sweep(pkv, dev, stream, read_gbs, K, W, cpu_seconds):
         P = cfg.partition_tokens or 512
 
         def rec(name, fn, nbytes, same_buffer=False, extra=None):
-            r = timed(fn, K, W, stream)
+            r = timed(fn, K, W, stream, settle_ms)
             d = {"bytes": nbytes, "avg_us": round(r["region_us"], 3), "wall_us": round(r["wall_us"], 3),
                  "median_us": round(r["median_us"], 3), "p10_us": round(r["p10_us"], 3),
                  "p90_us": round(r["p90_us"], 3)}
@@ -406,7 +413,7 @@ def config_sweep(pkv, dev, stream, read_gbs, K, W, cpu_seconds):
             if extra:
                 d.update(extra)
             if same_buffer:
-                r2 = timed(lambda i: fn(0), K, W, stream)
+                r2 = timed(lambda i: fn(0), K, W, stream, settle_ms)
                 d["same_buffer_avg_us"] = round(r2["region_us"], 3)
                 d["same_buffer_gbs"] = round(nbytes / (r2["region_us"] * 1e-6) / 1e9, 1)
             entry["paths"][name] = d
@@ -655,7 +662,7 @@ def main():
         pools = None
         torch.cuda.empty_cache()
         configs = config_sweep(pkv, dev, stream, calib["read_stream"]["gbs"], args.config_steps,
-                               args.config_warmup, args.cpu_seconds)
+                               args.config_warmup, args.cpu_seconds, args.settle_ms)
 
     cpu = None
     if args.cpu_seconds > 0:
