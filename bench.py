@@ -15,7 +15,7 @@ several replicas so that no step finds the previous step's KV in the 256 MB Infi
 Timing: first a settle phase, untimed and reported on its own (`settle` in the line): real steps
 until --settle-ms of host time (200 ms by default) have passed, because the device needs some tens
 of milliseconds of continuous work to reach its steady clock and power state (after 10 steps the
-timed steps read about 2 us longer than after 200, on the same box; a decode loop runs in the
+timed steps read about 2 us longer than after 200, on the same device; a decode loop runs in the
 steady state).  Then W untimed warmup steps (200 by default), then the timed region, K steps
 launched back to back between two HIP
 events on the launch stream (their average is the step kernel's average launch duration, and the

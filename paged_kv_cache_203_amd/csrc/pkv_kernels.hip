@@ -838,7 +838,7 @@ __device__ inline int step_tiles(const StepParams& p, int b) {
 // the Llama-3-8B-shaped step, against 115.5 us at 8 and 118 us at 4; with PV on the matrix
 // cores 16 and 20 units measure the same), six when several waves share a head (24 units: with
 // PV on the matrix cores, 40.2 us for the Qwen2-7B-shaped step with its pairs of waves sharing
-// stages, against 41.7 at 16, and 41.1 against 41.8 on another box, where 32 and 40 gave 41.9
+// stages, against 41.7 at 16, and 41.1 against 41.8 on another device, where 32 and 40 gave 41.9
 // and 41.4).
 __device__ inline int start_units(int waves_per_head) { return waves_per_head == 1 ? 12 : 24; }
 
