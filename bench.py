@@ -140,7 +140,8 @@ def step_bytes(w, partition_tokens, path):
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "step_kernel_llama3-8b-bf16-b64_traffic.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_203_amd", "csrc", f)
                   for f in ("pkv_kernels.hip", "pkv_device.h", "pkv_launch.h", "pkv_arrival.h",
-                            "pkv_prefix_body.h")]
+                            "pkv_prefix_body.h")] + \
+                 [os.path.join(ROOT, "paged_kv_cache_203_amd", "build.py")]   # the compile flags
 
 
 def kernel_source_hash():
