@@ -394,10 +394,10 @@ struct HeadPipe {
     for (int r0 = 0; r0 < 4; r0 += RPW) {
       u32x4 pv[RPW * NR];
       uint32_t vw[RPW][VW];   // this lane's V words of rows 4 rr + kq
-      LdsRows<Geo::VB> vr[RPW];
+      LdsRows<Geo::VB> vrows[RPW];
 #pragma unroll
       for (int j = 0; j < RPW; ++j) {
-        vr[j].read(vs + uint32_t(4 * (r0 + j)) * Geo::RB);
+        vrows[j].read(vs + uint32_t(4 * (r0 + j)) * Geo::RB);
 #pragma unroll
         for (int c = 0; c < NR; ++c)
           pv[j * NR + c] = lds_read16(p_lds + uint32_t((4 * (r0 + j) + kq) * GP + 4 * c) * 4u);
@@ -405,10 +405,10 @@ struct HeadPipe {
       lds_wait();
 #pragma unroll
       for (int j = 0; j < RPW; ++j) {
-        vr[j].pin();
+        vrows[j].pin();
 #pragma unroll
         for (int c = 0; c < NR; ++c) lds_pin(pv[j * NR + c]);
-        vr[j].words(vw[j]);
+        vrows[j].words(vw[j]);
       }
 #pragma unroll
       for (int j = 0; j < RPW; ++j) {
@@ -1010,10 +1010,10 @@ __device__ void step_merge(const StepParams& p, const StepSplit& sp, int b, int 
         const int k = k0 + u;
         const bool ok = k < npc && (dense || (k < NT ? flags[k] != 0 : sp.tiles_in(w_lo + k, base, n) > 0));
 #pragma unroll
-        for (int k = 0; k < kCols; ++k) {
-          const int64_t row = int64_t(k0 + u) * a.hq + h[k];
-          ls[k][u] = ok ? dev_load(&p.ws_lse[row0 + row]) : neg_inf();
-          vs[k][u] = ok ? dev_load16(rows, uint32_t(row * D + d0[k]) * 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int c = 0; c < kCols; ++c) {
+          const int64_t row = int64_t(k) * a.hq + h[c];
+          ls[c][u] = ok ? dev_load(&p.ws_lse[row0 + row]) : neg_inf();
+          vs[c][u] = ok ? dev_load16(rows, uint32_t(row * D + d0[c]) * 4) : f32x4{0.f, 0.f, 0.f, 0.f};
         }
       }
     };
@@ -1062,10 +1062,10 @@ __device__ void step_merge(const StepParams& p, const StepSplit& sp, int b, int 
       const int c = c0 + k * NT;
       if (c >= ncol) continue;
       const int64_t row = MQ ? step_row(p, b, h[k]) : int64_t(b) * a.hq + h[k];
-      const int64_t base = row * D + d0[k];
+      const int64_t obase = row * D + d0[k];
       const bool empty = MQ && !(l[k] > 0.f);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) store_elem<DT>(p.out, base + j, empty ? 0.f : o[k][j] / l[k]);
+      for (int j = 0; j < 4; ++j) store_elem<DT>(p.out, obase + j, empty ? 0.f : o[k][j] / l[k]);
       if (d0[k] == 0 && p.lse_out)
         p.lse_out[row] = empty ? neg_inf() : m[k] + __builtin_amdgcn_logf(l[k]) * kLn2;
     }
